@@ -1,0 +1,129 @@
+"""Seeded synthetic inputs for the W4A16 dequantize-GEMM.
+
+This module only draws random numbers and lays them out in the canonical
+input format; it holds none of the method's arithmetic (no dequantization,
+no product).  Both the GPU tests/benchmark and the CPU oracle take their
+inputs from here, and from nowhere else.
+
+Canonical format:
+  X        uint16 bit patterns [M][K] of fp16 or bf16, row-major
+  qweight  uint32 [K/8][N]; nibble i (bits 4i..4i+3) of word [r][n] is the
+           4-bit weight at k = 8r + i, column n
+  scales   uint16 bit patterns [K/G][N], same dtype as X
+  zeros    uint8 [K/G][N], values 0..15 (None for the symmetric format,
+           whose zero point is fixed at 8)
+
+Recipe (the workloads of the pages: decode of a 70B-class model, whose
+hidden size is 8192 and FFN size 28672):
+  * numpy Generator(PCG64); SeedSequence(seed).spawn(5) gives independent
+    streams for [X, q, scales, zeros, outlier columns].
+  * X ~ N(0, 1) drawn in float64, optionally with round(frac*K) distinct
+    "outlier" columns of K (chosen without replacement) multiplied by 20,
+    then rounded to the dtype (fp16: float64 -> float16 RNE; bf16:
+    float64 -> float32 -> bfloat16, both RNE).
+  * q ~ uniform integers 0..15.
+  * scale ~ U(0.002, 0.02) drawn in float64, rounded to the dtype like X.
+  * zero ~ uniform integers 0..15 (asymmetric) or none (symmetric).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+
+__all__ = ["Problem", "make_problem", "pack_nibbles", "to_dtype_bits", "WORKLOADS",
+           "workload"]
+
+
+def to_dtype_bits(x64: np.ndarray, dtype: str) -> np.ndarray:
+    """float64 array -> uint16 bit patterns of fp16 or bf16 (round to nearest even)."""
+    if dtype == "fp16":
+        return np.asarray(x64, dtype=np.float64).astype(np.float16).view(np.uint16)
+    if dtype == "bf16":
+        f32 = np.asarray(x64, dtype=np.float64).astype(np.float32)
+        u = f32.view(np.uint32).astype(np.uint64)
+        # round-to-nearest-even on the low 16 bits (inputs here are finite)
+        u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+        return u.astype(np.uint16)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def pack_nibbles(q: np.ndarray) -> np.ndarray:
+    """q[K][N] (values 0..15) -> qweight[K/8][N] uint32, nibble i = row 8r+i."""
+    K, N = q.shape
+    if K % 8:
+        raise ValueError("K must be a multiple of 8")
+    q8 = np.asarray(q, dtype=np.uint32).reshape(K // 8, 8, N)
+    out = np.zeros((K // 8, N), dtype=np.uint32)
+    for i in range(8):
+        out |= q8[:, i, :] << np.uint32(4 * i)
+    return out
+
+
+@dataclass
+class Problem:
+    M: int
+    K: int
+    N: int
+    G: int
+    dtype: str
+    sym: bool
+    X: np.ndarray                 # uint16 [M][K]
+    qweight: np.ndarray           # uint32 [K/8][N]
+    scales: np.ndarray            # uint16 [K/G][N]
+    zeros: Optional[np.ndarray]   # uint8 [K/G][N] or None
+    q: Optional[np.ndarray] = field(default=None, repr=False)   # uint8 [K][N] if kept
+
+
+def make_problem(M: int, K: int, N: int, G: int = 128, dtype: str = "fp16",
+                 sym: bool = False, seed: int = 0, outlier_frac: float = 0.0,
+                 outlier_mult: float = 20.0, keep_q: bool = False,
+                 scale_range=(0.002, 0.02)) -> Problem:
+    if K % 8 or K % G:
+        raise ValueError("K must be a multiple of 8 and of G")
+    streams = [np.random.Generator(np.random.PCG64(s))
+               for s in np.random.SeedSequence(seed).spawn(5)]
+    x64 = streams[0].standard_normal((M, K))
+    if outlier_frac > 0:
+        n_out = int(round(outlier_frac * K))
+        if n_out > 0:
+            cols = streams[4].choice(K, size=n_out, replace=False)
+            x64[:, cols] *= outlier_mult
+    X = to_dtype_bits(x64, dtype)
+    del x64
+    q = streams[1].integers(0, 16, size=(K, N), dtype=np.uint8)
+    qweight = pack_nibbles(q)
+    s64 = streams[2].uniform(scale_range[0], scale_range[1], size=(K // G, N))
+    scales = to_dtype_bits(s64, dtype)
+    zeros = None if sym else streams[3].integers(0, 16, size=(K // G, N), dtype=np.uint8)
+    return Problem(M, K, N, G, dtype, bool(sym), X, qweight, scales, zeros,
+                   q if keep_q else None)
+
+
+# Named workloads (shapes of a 70B-class decoder layer; "outliers" marks the
+# 0.1%-of-K-columns x20 activation pattern).
+WORKLOADS = {
+    "decode_m1_k4096_n4096_fp16_asym_g128":
+        dict(M=1, K=4096, N=4096, G=128, dtype="fp16", sym=False),
+    **{f"decode_m{m}_k8192_n28672_fp16_asym_g128_outliers":
+       dict(M=m, K=8192, N=28672, G=128, dtype="fp16", sym=False, outlier_frac=0.001)
+       for m in (1, 4, 8)},
+    **{f"decode_m{m}_k8192_n8192_fp16_asym_g128_outliers":
+       dict(M=m, K=8192, N=8192, G=128, dtype="fp16", sym=False, outlier_frac=0.001)
+       for m in (1, 4, 8)},
+    **{f"transition_m{m}_k8192_n28672_bf16_sym_g128":
+       dict(M=m, K=8192, N=28672, G=128, dtype="bf16", sym=True) for m in (16, 32)},
+    **{f"transition_m{m}_k28672_n8192_bf16_sym_g128":
+       dict(M=m, K=28672, N=8192, G=128, dtype="bf16", sym=True) for m in (16, 32)},
+    **{f"batch_m{m}_k8192_n28672_fp16_asym_g{g}":
+       dict(M=m, K=8192, N=28672, G=g, dtype="fp16", sym=False)
+       for m in (64, 128) for g in (64, 32)},
+    **{f"prefill_m{m}_k8192_n{n}_bf16_asym_g128":
+       dict(M=m, K=8192, N=n, G=128, dtype="bf16", sym=False)
+       for m in (4096, 8192) for n in (8192, 28672)},
+}
+
+
+def workload(name: str, seed: int = 0, keep_q: bool = False) -> Problem:
+    return make_problem(seed=seed, keep_q=keep_q, **WORKLOADS[name])
