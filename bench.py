@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused W4A16 dequantize-GEMM on one MI355X.
+
+One step = one w4a16_gemm call (the whole hot path: weight stream, unpack,
+group dequant, MFMA, reduction, epilogue) on a seeded synthetic workload.
+Inputs are resident in HBM before the timed region.  Every weight set fits
+in the 256 MB Infinity Cache, so the benchmark rotates over enough
+independent copies of the packed weights (>= 1 GiB in total) that each call
+reads its weights from HBM, as a decode step does when the other layers'
+weights have passed through the cache in between.
+
+Prints one JSON line (rank 0): metric, value, roofline, cpu_baseline, ...
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import w4a16_synth as synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
+MFMA_PEAK_TFLOPS = 2500.0    # MI355X dense fp16/bf16 MFMA, 2.5 PFLOP/s
+DEFAULT_WORKLOAD = "decode_m1_k8192_n28672_fp16_asym_g128_outliers"
+METRIC = "W4A16 GEMM achieved HBM GB/s"
+
+
+def algorithmic_bytes(cfg):
+    M, K, N, G = cfg["M"], cfg["K"], cfg["N"], cfg["G"]
+    b = K * N // 2 + (K // G) * N * 2 + M * K * 2 + M * N * 2
+    if not cfg["sym"]:
+        b += (K // G) * N // 2
+    return b
+
+
+def algorithmic_flops(cfg):
+    return 2 * cfg["M"] * cfg["N"] * cfg["K"]
+
+
+def bound_of(cfg):
+    # ridge of the MI355X roofline: 2.5e15 / 8e12 = 312.5 flop/byte
+    return "mfma" if algorithmic_flops(cfg) / algorithmic_bytes(cfg) > 312.5 else "hbm"
+
+
+def cpu_baseline(name, cfg, budget_s=12.0):
+    """The oracle as it stands, on this host's cores, on a slice of output
+    columns of the same workload; the rate is extrapolated to the whole N."""
+    import oracle
+
+    oracle.build()
+    threads = os.cpu_count() or 1
+    p = synth.workload(name)
+    M, K, N, G = cfg["M"], cfg["K"], cfg["N"], cfg["G"]
+    rows = min(M, 64)
+
+    def run(ncol):
+        qw = np.ascontiguousarray(p.qweight[:, :ncol])
+        sc = np.ascontiguousarray(p.scales[:, :ncol])
+        zr = None if p.zeros is None else np.ascontiguousarray(p.zeros[:, :ncol])
+        t0 = time.perf_counter()
+        oracle.gemm(p.X[:rows], qw, sc, zr, rows, ncol, K, G, cfg["dtype"], cfg["sym"],
+                    nthreads=threads)
+        return time.perf_counter() - t0
+
+    probe = min(N, max(threads, 64))
+    t_probe = run(probe)
+    ncol = int(min(N, max(probe, probe * budget_s / max(t_probe, 1e-6))))
+    t = run(ncol) if ncol > probe else t_probe
+    t_full = t * (N / ncol) * (M / rows)
+    return {
+        "value": round(algorithmic_bytes(cfg) / t_full / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{rows} of {M} rows x {ncol} of {N} columns (K={K}) of the same workload, "
+                  f"{t:.1f} s on {threads} threads, rate extrapolated linearly to the full "
+                  f"{M}x{N} output ({t_full:.1f} s)",
+    }
+
+
+def run_workload(name, steps, warmup, rotate_bytes=1 << 30, with_cpu=True, comparators=True):
+    import torch
+
+    import w4a16_dequant_gemm_amd as w4
+
+    w4.load_library()
+    cfg = dict(synth.WORKLOADS[name])
+    dev = torch.device("cuda:0")
+    p = synth.workload(name)
+    flags = w4.flags_of(p.dtype, p.sym)
+    X, qw, sc, zr = w4.to_device(p, dev)
+    base = w4.w4a16_repack(qw, sc, zr, p.K, p.N, p.G, flags)
+    del qw, sc, zr
+    copies = max(2, min(16, math.ceil(rotate_bytes / base.data.numel())))
+    blobs = [base] + [w4.PackedW4(base.data.clone(), base.K, base.N, base.group_size, base.flags,
+                                  base.layout_version) for _ in range(copies - 1)]
+    Y = torch.empty((p.M, p.N), dtype=X.dtype, device=dev)
+    ws = w4.workspace_for(w4.w4a16_workspace_bytes(p.M, p.N, p.K, p.G, flags), dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        w4.w4a16_gemm(X, blobs[i % copies], Y=Y, workspace=ws, stream=stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t0.elapsed_time(t1)
+    ms_step = ms_total / steps
+    per_launch = np.array([a.elapsed_time(b) for a, b in ev])
+    kern_ms = float(np.mean(per_launch))
+
+    nbytes = algorithmic_bytes(cfg)
+    flops = algorithmic_flops(cfg)
+    bound = bound_of(cfg)
+    if bound == "hbm":
+        achieved = nbytes / (kern_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        achieved = flops / (kern_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_TFLOPS, 4), "traffic": None}
+    out = {
+        "metric": METRIC,
+        "value": round(nbytes / (ms_step * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16" if p.dtype == "fp16" else "bf16",
+        "data": "synthetic",
+        "config": {"workload": name, "M": p.M, "K": p.K, "N": p.N, "group_size": p.G,
+                   "act_dtype": p.dtype, "quant": "sym" if p.sym else "asym",
+                   "outlier_cols": cfg.get("outlier_frac", 0.0), "parallelism": "none (1 GPU)",
+                   "cold_weight_copies": copies},
+        "kernel_us": round(kern_ms * 1e3, 3),
+        "kernel_us_p10_p50_p90": [round(float(np.percentile(per_launch, q)) * 1e3, 3)
+                                  for q in (10, 50, 90)],
+        "tflops": round(flops / (kern_ms * 1e-3) / 1e12, 2),
+        "weight_only_gbs": round((p.K * p.N // 2) / (kern_ms * 1e-3) / 1e9, 1),
+        "roofline": roof,
+    }
+    if comparators:
+        out["comparators"] = comparator_times(p, X, blobs, copies, stream)
+    if with_cpu:
+        out["cpu_baseline"] = cpu_baseline(name, cfg)
+    return out
+
+
+def comparator_times(p, X, blobs, copies, stream, reps=20):
+    """Context, not the metric: a dense fp16/bf16 torch.matmul (hipBLASLt) on the
+    same shape, and the unfused route (dequantize to HBM, then torch.matmul)."""
+    import torch
+
+    import w4a16_dequant_gemm_amd as w4
+
+    res = {}
+    try:
+        Wd = [w4.w4a16_dequant(blobs[i]) for i in range(min(copies, 4))]
+        torch.cuda.synchronize()
+
+        def timeit(fn):
+            for i in range(3):
+                fn(i)
+            torch.cuda.synchronize()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for i in range(reps):
+                fn(i)
+            b.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / reps * 1e3
+
+        res["dense_matmul_us"] = round(timeit(lambda i: torch.matmul(X, Wd[i % len(Wd)])), 3)
+        res["unfused_dequant_then_matmul_us"] = round(
+            timeit(lambda i: torch.matmul(X, w4.w4a16_dequant(blobs[i % copies]))), 3)
+        res["note"] = ("dense W held in HBM, rotated over %d copies; unfused writes the "
+                       "dequantized W to HBM then multiplies" % len(Wd))
+        del Wd
+    except RuntimeError as e:   # e.g. out of memory for the dense copies
+        res["error"] = str(e)[:200]
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
+                    help="a name from w4a16_synth.WORKLOADS, or 'all' (one line each)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-comparators", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the W4A16 path "
+                                   "has no multi-GPU mode (see the sharding notes in DESIGN.md)",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+    names = list(synth.WORKLOADS) if args.workload == "all" else [args.workload]
+    for name in names:
+        out = run_workload(name, args.steps, args.warmup,
+                           with_cpu=not args.no_cpu and args.workload != "all",
+                           comparators=not args.no_comparators)
+        print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

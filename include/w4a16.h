@@ -1,0 +1,163 @@
+/*
+ * w4a16.h -- C ABI of the MI355X (gfx950) fused W4A16 dequantize-GEMM library.
+ *
+ *   Y[M][N] = X[M][K] . deq[K][N],   deq[k][n] = RNE((q[k][n] - z[g][n]) * s[g][n]),
+ *   g = floor(k / G), fp32 accumulation, Y rounded to the activation dtype.
+ *
+ * The method: page "W4A16 GEMM 算子浅析：INT4 权重反量化的计算流水线"
+ * (nxmr.cn), section "计算流水线的核心哲学" -- 4-bit weights stay packed in
+ * HBM, are unpacked and dequantized (weight minus zero, times scale) in
+ * registers, and only then feed the matrix unit with fp32 accumulation; and
+ * page "量化开销对比：各家方案的矩阵乘账本与省账手段" (laojiahuo2003.github.io),
+ * section 6: one launch, one pass over the weights, nothing materialised in
+ * between (6.1); the group scale multiplies the weight operand before the
+ * multiply-accumulate because it changes along k (6.2); weights, scales and
+ * zeros are repacked offline into the kernel's order (6.4).
+ *
+ * Conventions for every entry point:
+ *   - Plain C types only; no exception crosses the ABI.
+ *   - "dev" pointers are device memory on the current HIP device; the caller
+ *     owns every buffer.  The library never allocates, frees or synchronizes.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued asynchronously on it; no host<->device copies are made,
+ *     so calls may be captured into a HIP graph.
+ *   - Every argument is validated on the host before any HIP call.  A call
+ *     that fails validation launches nothing and writes nothing.  A launch
+ *     error reported by HIP is returned as W4A16_ERR_HIP.
+ *   - Supported shapes: M >= 1; K >= 1 with K % G == 0; N >= 1 with N % 128 == 0
+ *     (other N: W4A16_ERR_UNSUPPORTED); G in {32, 64, 128} (other G:
+ *     W4A16_ERR_UNSUPPORTED); M, N, K < 2^31 and K*N < 2^40.
+ *   - Every dev pointer must be 16-byte aligned.
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define W4A16_ABI_VERSION 1
+#define W4A16_LAYOUT_VERSION 1
+
+typedef enum {
+    W4A16_OK = 0,
+    W4A16_ERR_INVALID_ARG = 1,   /* bad shape, NULL/misaligned pointer, bad flags, short buffer */
+    W4A16_ERR_UNSUPPORTED = 2,   /* valid request outside what this build implements */
+    W4A16_ERR_WORKSPACE = 3,     /* workspace missing or smaller than w4a16_workspace_bytes() */
+    W4A16_ERR_HIP = 4            /* the HIP runtime reported an error at launch */
+} w4a16_status_t;
+
+/* flags bitfield */
+#define W4A16_FP16 0x0u   /* X, scales and Y are IEEE binary16 */
+#define W4A16_BF16 0x1u   /* X, scales and Y are bfloat16 */
+#define W4A16_ASYM 0x0u   /* zeros: uint8 [K/G][N], values 0..15 */
+#define W4A16_SYM  0x2u   /* zero point fixed at 8; the zeros pointer must be NULL */
+#define W4A16_FLAGS_MASK 0x3u
+
+/* W4A16_ABI_VERSION of the loaded library. */
+int w4a16_abi_version(void);
+
+/* W4A16_LAYOUT_VERSION: the format of the repacked blob.  A blob is only
+ * valid for a library with the same layout version. */
+int w4a16_layout_version(void);
+
+/* Static, NUL-terminated description of a status code. */
+const char *w4a16_status_string(w4a16_status_t status);
+
+/*
+ * Size in bytes of the repacked blob for (K, N, G, flags), or 0 if the shape
+ * is invalid or unsupported.  It is exactly the algorithmic byte count of the
+ * quantized weight: K*N/2 (packed nibbles) + (K/G)*N*2 (scales) +
+ * (K/G)*N/2 (zeros, asymmetric only).
+ */
+size_t w4a16_packed_bytes(int64_t K, int64_t N, int group_size, uint32_t flags);
+
+/*
+ * Offline repack of the canonical tensors into the kernels' tile order.
+ * Page "量化开销对比", section 6.4: scales and zeros stored in natural group
+ * order would cost one scattered global read per weight tile; they are laid
+ * next to the weights in consumption order instead.  Not on the per-token path.
+ *
+ *   qweight  dev, uint32 [K/8][N] row-major; nibble i (bits 4i..4i+3) of word
+ *            [r][n] is q[8r+i][n] (least-significant nibble first).
+ *   scales   dev, [K/G][N] row-major, fp16 or bf16 per flags.
+ *   zeros    dev, uint8 [K/G][N] row-major, values 0..15 (asymmetric);
+ *            must be NULL when flags has W4A16_SYM.
+ *   packed   dev, output, packed_bytes >= w4a16_packed_bytes(K, N, G, flags).
+ * Errors: INVALID_ARG (shape, pointers, flags, SYM/zeros mismatch, short
+ * packed_bytes), UNSUPPORTED (N % 128, G), HIP.
+ */
+w4a16_status_t w4a16_repack(const uint32_t *qweight, const void *scales, const uint8_t *zeros,
+                            int64_t K, int64_t N, int group_size, uint32_t flags,
+                            void *packed, size_t packed_bytes, void *stream);
+
+/*
+ * Exact inverse of w4a16_repack (for round-trip checks and export): writes
+ * the canonical qweight, scales and (asymmetric) zeros back from a blob.
+ * Same argument rules as w4a16_repack, with the directions reversed.
+ */
+w4a16_status_t w4a16_unrepack(const void *packed, size_t packed_bytes, uint32_t *qweight,
+                              void *scales, uint8_t *zeros, int64_t K, int64_t N,
+                              int group_size, uint32_t flags, void *stream);
+
+/*
+ * Workspace bytes w4a16_gemm needs for this problem (0 = none).  The value
+ * depends on the kernel variant and split-K factor chosen for the shape; it is
+ * at most 4 KiB + 64 * M_pad * N bytes, M_pad = M rounded up to 32.
+ */
+size_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int group_size, uint32_t flags);
+
+/*
+ * The fused product Y = X . deq(packed), fp32 accumulation, Y rounded to
+ * nearest even into the activation dtype.  One pass over the packed weights;
+ * dequantized weights exist only in registers.
+ *
+ *   X          dev, [M][K] row-major, fp16 or bf16 per flags.
+ *   packed     dev, blob from w4a16_repack with the same K, N, G and flags.
+ *   Y          dev, output [M][N] row-major, same dtype as X.  Must not overlap
+ *              X, packed or workspace.
+ *   workspace  dev, >= w4a16_workspace_bytes(M, N, K, G, flags) bytes (may be
+ *              NULL when that is 0).  It must be zero-filled before its first
+ *              use; every call leaves its counters zero again, so one
+ *              zero-fill suffices for any number of calls.  Calls that share a
+ *              workspace must not run concurrently.
+ * Kernel choice: small M uses a split-K streaming kernel whose partial sums
+ * are reduced in a fixed order (results are bitwise reproducible run to run);
+ * larger M uses an LDS-tiled MFMA kernel.  Both use v_mfma_f32_32x32x16.
+ * The environment variables W4A16_FORCE_VARIANT=splitk|tiled and
+ * W4A16_SPLITS=<n> override the choice (benchmarking only; they also change
+ * w4a16_workspace_bytes).
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.
+ */
+w4a16_status_t w4a16_gemm(const void *X, const void *packed, size_t packed_bytes, void *Y,
+                          int64_t M, int64_t N, int64_t K, int group_size, uint32_t flags,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Test and export aid: writes deq[K][N] row-major (activation dtype) from a
+ * blob, using the same device dequantization code as w4a16_gemm.  This is the
+ * materialising "route B" the fused path avoids (page "量化开销对比",
+ * section 3); it exists for bit-exact checks and for the unfused comparator.
+ */
+w4a16_status_t w4a16_dequant(const void *packed, size_t packed_bytes, void *W_out,
+                             int64_t K, int64_t N, int group_size, uint32_t flags,
+                             void *stream);
+
+/*
+ * Diagnostic: one v_mfma_f32_32x32x16 (fp16 or bf16 per flags) on A[32][16]
+ * and B[16][32] (row-major, dev), loaded into the operand registers the way
+ * the GEMM kernels load them, with D[32][32] (fp32, row-major, dev) written
+ * back the way the kernels read the accumulators.  D == A.B checks the
+ * operand and accumulator layouts the kernels rely on.
+ */
+w4a16_status_t w4a16_mfma_layout_probe(const void *A, const void *B, float *D, uint32_t flags,
+                                       void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */

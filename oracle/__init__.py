@@ -31,7 +31,7 @@ def build(force: bool = False) -> str:
     """Compile the C oracle into ``oracle/liboracle.so`` with gcc."""
     if force or not os.path.exists(_LIB):
         tmp = _LIB + f".tmp{os.getpid()}"
-        cmd = ["gcc", "-O2", "-std=c11", "-D_DEFAULT_SOURCE", "-shared", "-fPIC",
+        cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-D_DEFAULT_SOURCE", "-shared", "-fPIC",
                "-pthread", _SRC, "-o", tmp, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB)

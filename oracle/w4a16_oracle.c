@@ -42,7 +42,7 @@
  *   scales   uint16 bit patterns [K/G][N] (same dtype as X)
  *   zeros    uint8 [K/G][N], values 0..15; ignored when sym != 0
  *
- * Build: gcc -O2 -shared -fPIC -pthread w4a16_oracle.c -lm
+ * Build: gcc -O2 -ffp-contract=off -shared -fPIC -pthread w4a16_oracle.c -lm
  */
 #include <math.h>
 #include <pthread.h>

@@ -1,0 +1,240 @@
+"""Python binding of the MI355X fused W4A16 dequantize-GEMM library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libw4a16.so`` (built from ``csrc/`` by ``build.py``).  PyTorch
+provides device memory and the current stream.  There is no fallback: if the
+library is missing, importing the C functions raises.
+
+The functions carry the names of the C entry points in ``include/w4a16.h``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libw4a16.so")
+
+W4A16_OK = 0
+W4A16_ERR_INVALID_ARG = 1
+W4A16_ERR_UNSUPPORTED = 2
+W4A16_ERR_WORKSPACE = 3
+W4A16_ERR_HIP = 4
+
+W4A16_FP16 = 0x0
+W4A16_BF16 = 0x1
+W4A16_ASYM = 0x0
+W4A16_SYM = 0x2
+
+# entry points declared in include/w4a16.h
+C_FUNCTIONS = (
+    "w4a16_abi_version", "w4a16_layout_version", "w4a16_status_string", "w4a16_packed_bytes",
+    "w4a16_repack", "w4a16_unrepack", "w4a16_workspace_bytes", "w4a16_gemm", "w4a16_dequant",
+    "w4a16_mfma_layout_probe",
+)
+
+
+class W4A16Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libw4a16.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m "
+                           "w4a16_dequant_gemm_amd.build` (or __graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    p, i64, ci, u32, sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint32,
+                           ctypes.c_size_t)
+    lib.w4a16_abi_version.restype = ci
+    lib.w4a16_layout_version.restype = ci
+    lib.w4a16_status_string.argtypes = [ci]
+    lib.w4a16_status_string.restype = ctypes.c_char_p
+    lib.w4a16_packed_bytes.argtypes = [i64, i64, ci, u32]
+    lib.w4a16_packed_bytes.restype = sz
+    lib.w4a16_repack.argtypes = [p, p, p, i64, i64, ci, u32, p, sz, p]
+    lib.w4a16_repack.restype = ci
+    lib.w4a16_unrepack.argtypes = [p, sz, p, p, p, i64, i64, ci, u32, p]
+    lib.w4a16_unrepack.restype = ci
+    lib.w4a16_workspace_bytes.argtypes = [i64, i64, i64, ci, u32]
+    lib.w4a16_workspace_bytes.restype = sz
+    lib.w4a16_gemm.argtypes = [p, p, sz, p, i64, i64, i64, ci, u32, p, sz, p]
+    lib.w4a16_gemm.restype = ci
+    lib.w4a16_dequant.argtypes = [p, sz, p, i64, i64, ci, u32, p]
+    lib.w4a16_dequant.restype = ci
+    lib.w4a16_mfma_layout_probe.argtypes = [p, p, p, u32, p]
+    lib.w4a16_mfma_layout_probe.restype = ci
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().w4a16_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != W4A16_OK:
+        raise W4A16Error(status, where)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def flags_of(dtype: str, sym: bool) -> int:
+    return (W4A16_BF16 if dtype in ("bf16", "bfloat16") else W4A16_FP16) | (W4A16_SYM if sym else 0)
+
+
+def torch_dtype(flags: int) -> torch.dtype:
+    return torch.bfloat16 if flags & W4A16_BF16 else torch.float16
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+
+def w4a16_abi_version() -> int:
+    return load_library().w4a16_abi_version()
+
+
+def w4a16_layout_version() -> int:
+    return load_library().w4a16_layout_version()
+
+
+def w4a16_packed_bytes(K: int, N: int, group_size: int, flags: int) -> int:
+    return int(load_library().w4a16_packed_bytes(K, N, group_size, flags))
+
+
+def w4a16_workspace_bytes(M: int, N: int, K: int, group_size: int, flags: int) -> int:
+    return int(load_library().w4a16_workspace_bytes(M, N, K, group_size, flags))
+
+
+@dataclass
+class PackedW4:
+    """A repacked weight blob and the parameters it was made for."""
+    data: torch.Tensor          # uint8 device tensor
+    K: int
+    N: int
+    group_size: int
+    flags: int
+    layout_version: int
+
+
+def w4a16_repack(qweight: torch.Tensor, scales: torch.Tensor, zeros: Optional[torch.Tensor],
+                 K: int, N: int, group_size: int, flags: int, stream=None) -> PackedW4:
+    nbytes = w4a16_packed_bytes(K, N, group_size, flags)
+    if nbytes == 0:
+        raise W4A16Error(W4A16_ERR_UNSUPPORTED if N % 128 else W4A16_ERR_INVALID_ARG,
+                         "w4a16_packed_bytes")
+    packed = torch.empty(nbytes, dtype=torch.uint8, device=qweight.device)
+    _check(load_library().w4a16_repack(_ptr(qweight), _ptr(scales), _ptr(zeros), K, N,
+                                       group_size, flags, _ptr(packed), nbytes, _stream(stream)),
+           "w4a16_repack")
+    return PackedW4(packed, K, N, group_size, flags, w4a16_layout_version())
+
+
+def w4a16_unrepack(packed: PackedW4, stream=None):
+    dev = packed.data.device
+    K, N, G, flags = packed.K, packed.N, packed.group_size, packed.flags
+    qweight = torch.empty((K // 8, N), dtype=torch.int32, device=dev)
+    scales = torch.empty((K // G, N), dtype=torch_dtype(flags), device=dev)
+    zeros = None if flags & W4A16_SYM else torch.empty((K // G, N), dtype=torch.uint8, device=dev)
+    _check(load_library().w4a16_unrepack(_ptr(packed.data), packed.data.numel(), _ptr(qweight),
+                                         _ptr(scales), _ptr(zeros), K, N, G, flags,
+                                         _stream(stream)), "w4a16_unrepack")
+    return qweight, scales, zeros
+
+
+_workspaces = {}
+
+
+def workspace_for(nbytes: int, device: torch.device) -> Optional[torch.Tensor]:
+    """A zero-filled workspace of at least nbytes, cached per device (the library
+    leaves its counters zero after every call)."""
+    if nbytes == 0:
+        return None
+    key = (device.type, device.index)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def w4a16_gemm(X: torch.Tensor, packed: PackedW4, M: Optional[int] = None,
+               Y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+               stream=None) -> torch.Tensor:
+    """Y[M][N] = X[M][K] . dequant(packed); X is [M][K] fp16/bf16 on the device."""
+    if packed.layout_version != w4a16_layout_version():
+        raise W4A16Error(W4A16_ERR_INVALID_ARG, "w4a16_gemm (blob layout version)")
+    K, N, G, flags = packed.K, packed.N, packed.group_size, packed.flags
+    if M is None:
+        M = X.shape[0]
+    if X.dtype != torch_dtype(flags) or X.numel() != M * K or not X.is_contiguous():
+        raise W4A16Error(W4A16_ERR_INVALID_ARG, "w4a16_gemm (X dtype/shape)")
+    if Y is None:
+        Y = torch.empty((M, N), dtype=X.dtype, device=X.device)
+    need = w4a16_workspace_bytes(M, N, K, G, flags)
+    if workspace is None:
+        workspace = workspace_for(need, X.device)
+    _check(load_library().w4a16_gemm(_ptr(X), _ptr(packed.data), packed.data.numel(), _ptr(Y),
+                                     M, N, K, G, flags, _ptr(workspace),
+                                     0 if workspace is None else workspace.numel(),
+                                     _stream(stream)), "w4a16_gemm")
+    return Y
+
+
+def w4a16_dequant(packed: PackedW4, W_out: Optional[torch.Tensor] = None,
+                  stream=None) -> torch.Tensor:
+    K, N = packed.K, packed.N
+    if W_out is None:
+        W_out = torch.empty((K, N), dtype=torch_dtype(packed.flags), device=packed.data.device)
+    _check(load_library().w4a16_dequant(_ptr(packed.data), packed.data.numel(), _ptr(W_out), K,
+                                        N, packed.group_size, packed.flags, _stream(stream)),
+           "w4a16_dequant")
+    return W_out
+
+
+def w4a16_mfma_layout_probe(A: torch.Tensor, B: torch.Tensor, flags: int,
+                            stream=None) -> torch.Tensor:
+    D = torch.empty((32, 32), dtype=torch.float32, device=A.device)
+    _check(load_library().w4a16_mfma_layout_probe(_ptr(A), _ptr(B), _ptr(D), flags,
+                                                  _stream(stream)), "w4a16_mfma_layout_probe")
+    return D
+
+
+# ---------------------------------------------------------------------------
+# host <-> device plumbing for the canonical numpy tensors of w4a16_synth
+# ---------------------------------------------------------------------------
+
+def to_device(problem, device="cuda"):
+    """Canonical numpy tensors of a w4a16_synth.Problem -> device tensors."""
+    tdt = torch.bfloat16 if problem.dtype == "bf16" else torch.float16
+    X = torch.from_numpy(problem.X.view("int16")).view(tdt).to(device)
+    qw = torch.from_numpy(problem.qweight.view("int32")).to(device)
+    sc = torch.from_numpy(problem.scales.view("int16")).view(tdt).to(device)
+    zr = None if problem.zeros is None else torch.from_numpy(problem.zeros).to(device)
+    return X, qw, sc, zr
+
+
+def bits_of(t: torch.Tensor):
+    """Device fp16/bf16 tensor -> numpy uint16 bit patterns."""
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view("uint16")

@@ -1,0 +1,236 @@
+// w4a16_api.cpp -- the extern "C" entry points declared in include/w4a16.h:
+// host-side validation (always before any HIP call), the kernel plan, and
+// the launches.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "../../include/w4a16.h"
+#include "w4a16_internal.h"
+
+namespace w4a16 {
+
+namespace {
+
+constexpr int kNumCUs = 256;        // MI355X compute units
+constexpr int kMaxSplits = 16;
+constexpr int kSplitKWaves = 8;     // waves per split-K workgroup
+constexpr int kSplitKBatch = 8;     // k-steps per split-K load batch
+constexpr int kTiledStage = 8;      // k-steps per tiled stage
+constexpr int64_t kMaxDim = (int64_t)1 << 31;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+int env_int(const char* name, int dflt) {
+    const char* v = getenv(name);
+    if (!v || !*v) return dflt;
+    char* end = nullptr;
+    long x = strtol(v, &end, 10);
+    return (end && *end == 0) ? (int)x : dflt;
+}
+
+// Shape checks shared by every entry point: 0 = ok, else a status.
+w4a16_status_t check_shape(int64_t K, int64_t N, int group_size, uint32_t flags) {
+    if (flags & ~W4A16_FLAGS_MASK) return W4A16_ERR_INVALID_ARG;
+    if (K < 1 || N < 1 || K >= kMaxDim || N >= kMaxDim) return W4A16_ERR_INVALID_ARG;
+    if (group_size != 32 && group_size != 64 && group_size != 128) {
+        // a group size that cannot divide K is an invalid request whatever the build
+        if (group_size < 1 || K % group_size != 0) return W4A16_ERR_INVALID_ARG;
+        return W4A16_ERR_UNSUPPORTED;
+    }
+    if (K % group_size != 0) return W4A16_ERR_INVALID_ARG;
+    if ((double)K * (double)N >= (double)((int64_t)1 << 40)) return W4A16_ERR_INVALID_ARG;
+    if (N % kColBlock != 0) return W4A16_ERR_UNSUPPORTED;
+    return W4A16_OK;
+}
+
+w4a16_status_t from_hip(hipError_t e) { return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP; }
+
+}  // namespace
+
+Plan make_plan(int64_t M, int64_t N, int64_t K, int G, uint32_t /*flags*/) {
+    Plan p;
+    memset(&p, 0, sizeof(p));
+    const int64_t KS = K / kKStep;
+    const int64_t NB = N / kColBlock;
+    const char* fv = getenv("W4A16_FORCE_VARIANT");
+    bool splitk = M <= 32;
+    if (fv && strcmp(fv, "splitk") == 0 && M <= 32) splitk = true;
+    if (fv && strcmp(fv, "tiled") == 0) splitk = false;
+    const int forced_splits = env_int("W4A16_SPLITS", 0);
+    (void)G;
+
+    if (splitk) {
+        p.variant = VARIANT_SPLITK;
+        p.mt = 1;
+        p.waves = kSplitKWaves;
+        // Choose the split count S: minimise rounds-of-workgroups x work per
+        // workgroup, with a small charge per split for the partial traffic.
+        int best_s = 1;
+        double best_cost = 1e300;
+        for (int s = 1; s <= kMaxSplits; ++s) {
+            const int64_t spw = round_up(ceil_div(KS, (int64_t)s * kSplitKWaves), kSplitKBatch);
+            const int64_t s_eff = ceil_div(KS, spw * kSplitKWaves);
+            const int64_t wgs = NB * s_eff;
+            const double rounds = (double)ceil_div(wgs, kNumCUs);
+            const double cost = rounds * (double)(spw * kSplitKWaves) + 2.0 * (double)s_eff;
+            if (cost < best_cost - 1e-9) {
+                best_cost = cost;
+                best_s = s;
+            }
+        }
+        if (forced_splits > 0) best_s = forced_splits < kMaxSplits ? forced_splits : kMaxSplits;
+        const int64_t spw = round_up(ceil_div(KS, (int64_t)best_s * kSplitKWaves), kSplitKBatch);
+        p.steps_per_split = (int)spw;
+        p.splits = (int)ceil_div(KS, spw * kSplitKWaves);
+        p.grid_x = (int)NB;
+        p.grid_y = p.splits;
+        p.grid_z = 1;
+        p.tiles = (int)NB;
+        const int64_t nq = ceil_div(M, 8);
+        p.tile_floats = (size_t)4 * nq * 64 * 4;
+    } else {
+        p.variant = VARIANT_TILED;
+        p.mt = M <= 64 ? 2 : 4;
+        p.waves = 4;
+        const int64_t CG = ceil_div(NB, 4);
+        const int64_t RB = ceil_div(M, 32 * p.mt);
+        const int64_t tiles = CG * RB;
+        const int64_t slots = (int64_t)kNumCUs * (p.mt == 2 ? 2 : 1);
+        int64_t s = 1;
+        if (tiles < slots) s = ceil_div(slots, tiles);
+        if (s > kMaxSplits) s = kMaxSplits;
+        if (forced_splits > 0) s = forced_splits < kMaxSplits ? forced_splits : kMaxSplits;
+        // at least 4 stages per split
+        int64_t sps = round_up(ceil_div(KS, s), kTiledStage);
+        if (sps < 4 * kTiledStage) sps = 4 * kTiledStage;
+        p.steps_per_split = (int)sps;
+        p.splits = (int)ceil_div(KS, sps);
+        p.grid_x = (int)CG;
+        p.grid_y = (int)RB;
+        p.grid_z = p.splits;
+        p.tiles = (int)tiles;
+        p.tile_floats = (size_t)4 * p.mt * 4 * 16 * 64;
+    }
+    if (p.splits > 1) {
+        p.counters_bytes = (size_t)round_up((int64_t)p.tiles * 4, 256);
+        p.workspace = p.counters_bytes + (size_t)p.tiles * p.splits * p.tile_floats * 4;
+    } else {
+        p.tiles = 0;
+        p.counters_bytes = 0;
+        p.workspace = 0;
+    }
+    return p;
+}
+
+}  // namespace w4a16
+
+using namespace w4a16;
+
+extern "C" {
+
+int w4a16_abi_version(void) { return W4A16_ABI_VERSION; }
+
+int w4a16_layout_version(void) { return W4A16_LAYOUT_VERSION; }
+
+const char* w4a16_status_string(w4a16_status_t s) {
+    switch (s) {
+        case W4A16_OK: return "ok";
+        case W4A16_ERR_INVALID_ARG: return "invalid argument";
+        case W4A16_ERR_UNSUPPORTED: return "unsupported shape or group size";
+        case W4A16_ERR_WORKSPACE: return "workspace missing or too small";
+        case W4A16_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+size_t w4a16_packed_bytes(int64_t K, int64_t N, int group_size, uint32_t flags) {
+    if (check_shape(K, N, group_size, flags) != W4A16_OK) return 0;
+    return make_layout(K, N, group_size, (flags & W4A16_SYM) != 0).total;
+}
+
+w4a16_status_t w4a16_repack(const uint32_t* qweight, const void* scales, const uint8_t* zeros,
+                            int64_t K, int64_t N, int group_size, uint32_t flags, void* packed,
+                            size_t packed_bytes, void* stream) {
+    w4a16_status_t st = check_shape(K, N, group_size, flags);
+    if (st != W4A16_OK) return st;
+    const bool sym = (flags & W4A16_SYM) != 0;
+    if (sym != (zeros == nullptr)) return W4A16_ERR_INVALID_ARG;
+    if (!qweight || !scales || !packed) return W4A16_ERR_INVALID_ARG;
+    if (!aligned16(qweight) || !aligned16(scales) || !aligned16(packed) ||
+        (zeros && !aligned16(zeros)))
+        return W4A16_ERR_INVALID_ARG;
+    const Layout L = make_layout(K, N, group_size, sym);
+    if (packed_bytes < L.total) return W4A16_ERR_INVALID_ARG;
+    return from_hip(launch_repack(qweight, scales, zeros, L, (flags & W4A16_BF16) != 0, packed,
+                                  (hipStream_t)stream));
+}
+
+w4a16_status_t w4a16_unrepack(const void* packed, size_t packed_bytes, uint32_t* qweight,
+                              void* scales, uint8_t* zeros, int64_t K, int64_t N, int group_size,
+                              uint32_t flags, void* stream) {
+    w4a16_status_t st = check_shape(K, N, group_size, flags);
+    if (st != W4A16_OK) return st;
+    const bool sym = (flags & W4A16_SYM) != 0;
+    if (sym != (zeros == nullptr)) return W4A16_ERR_INVALID_ARG;
+    if (!qweight || !scales || !packed) return W4A16_ERR_INVALID_ARG;
+    if (!aligned16(qweight) || !aligned16(scales) || !aligned16(packed) ||
+        (zeros && !aligned16(zeros)))
+        return W4A16_ERR_INVALID_ARG;
+    const Layout L = make_layout(K, N, group_size, sym);
+    if (packed_bytes < L.total) return W4A16_ERR_INVALID_ARG;
+    return from_hip(launch_unrepack(packed, L, (flags & W4A16_BF16) != 0, qweight, scales, zeros,
+                                    (hipStream_t)stream));
+}
+
+size_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int group_size, uint32_t flags) {
+    if (M < 1 || M >= kMaxDim || check_shape(K, N, group_size, flags) != W4A16_OK) return 0;
+    return make_plan(M, N, K, group_size, flags).workspace;
+}
+
+w4a16_status_t w4a16_gemm(const void* X, const void* packed, size_t packed_bytes, void* Y,
+                          int64_t M, int64_t N, int64_t K, int group_size, uint32_t flags,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    if (M < 1 || M >= kMaxDim) return W4A16_ERR_INVALID_ARG;
+    w4a16_status_t st = check_shape(K, N, group_size, flags);
+    if (st != W4A16_OK) return st;
+    if (!X || !packed || !Y) return W4A16_ERR_INVALID_ARG;
+    if (!aligned16(X) || !aligned16(packed) || !aligned16(Y)) return W4A16_ERR_INVALID_ARG;
+    if ((double)M * (double)K >= (double)((int64_t)1 << 40) ||
+        (double)M * (double)N >= (double)((int64_t)1 << 40))
+        return W4A16_ERR_INVALID_ARG;
+    const Layout L = make_layout(K, N, group_size, (flags & W4A16_SYM) != 0);
+    if (packed_bytes < L.total) return W4A16_ERR_INVALID_ARG;
+    const Plan plan = make_plan(M, N, K, group_size, flags);
+    if (plan.workspace > 0) {
+        if (!workspace || workspace_bytes < plan.workspace || !aligned16(workspace))
+            return W4A16_ERR_WORKSPACE;
+    }
+    return from_hip(launch_gemm(X, packed, Y, M, L, (flags & W4A16_BF16) != 0, plan, workspace,
+                                (hipStream_t)stream));
+}
+
+w4a16_status_t w4a16_dequant(const void* packed, size_t packed_bytes, void* W_out, int64_t K,
+                             int64_t N, int group_size, uint32_t flags, void* stream) {
+    w4a16_status_t st = check_shape(K, N, group_size, flags);
+    if (st != W4A16_OK) return st;
+    if (!packed || !W_out || !aligned16(packed) || !aligned16(W_out)) return W4A16_ERR_INVALID_ARG;
+    const Layout L = make_layout(K, N, group_size, (flags & W4A16_SYM) != 0);
+    if (packed_bytes < L.total) return W4A16_ERR_INVALID_ARG;
+    return from_hip(launch_dequant(packed, L, (flags & W4A16_BF16) != 0, W_out,
+                                   (hipStream_t)stream));
+}
+
+w4a16_status_t w4a16_mfma_layout_probe(const void* A, const void* B, float* D, uint32_t flags,
+                                       void* stream) {
+    if (flags & ~W4A16_BF16) return W4A16_ERR_INVALID_ARG;
+    if (!A || !B || !D || !aligned16(A) || !aligned16(B) || !aligned16(D))
+        return W4A16_ERR_INVALID_ARG;
+    return from_hip(launch_mfma_probe(A, B, D, (flags & W4A16_BF16) != 0, (hipStream_t)stream));
+}
+
+}  // extern "C"

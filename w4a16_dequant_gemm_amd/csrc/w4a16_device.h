@@ -1,0 +1,244 @@
+// w4a16_device.h -- gfx950 device helpers: in-register unpack + group dequant,
+// MFMA operand types, output rounding.
+//
+// Page "W4A16 GEMM 算子浅析" (nxmr.cn), sections "计算流水线的核心哲学" and
+// "Marlin 与 CUTLASS 中的寄存器解包黑魔法": split a 32-bit word into its eight
+// nibbles with masks and shifts, turn each nibble into a 16-bit float by
+// placing it in the fraction field of a float whose spacing is 1 (no
+// integer-to-float convert instruction), then subtract the zero point and
+// multiply by the group scale before the values enter the matrix unit.
+// Page "量化开销对比", section 6.3: the unpacked values must land directly in
+// the operand registers the matrix instruction expects.
+//
+// Rounding: each dequantized weight is RNE((q - z) * s) in the activation
+// dtype, the single rounding of the exact product.
+//   fp16: (1024+q) - (1024+z) and (64+q) - (64+z) are exact small integers in
+//         fp16, so v_pk_add_f16 is exact and v_pk_mul_f16 rounds once.  (A
+//         fused multiply-add against a pre-multiplied zero would round the
+//         addend first and is not exact.)
+//   bf16: there is no packed bf16 arithmetic on gfx950, so each value goes
+//         through fp32: fma(q, s, -z*s) is exact (|q - z| <= 15 has 4 bits, s
+//         has 8 significant bits, and -z*s is itself exact), then
+//         v_cvt_pk_bf16_f32 rounds once per value.  When -z*s overflows fp32
+//         (scales above about 2.3e37) a wave switches to (q - z) * s, also
+//         exact before the one rounding.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4a16 {
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+enum { DT_F16 = 0, DT_BF16 = 1 };
+
+// Per-column dequantization constants for one group.
+template <int DT>
+struct ColParams;
+
+template <>
+struct ColParams<DT_F16> {
+    uint32_t s2;   // (s, s) as two fp16
+    uint32_t bA;   // (1024+z, 1024+z): bias of pairs taken with mask 0x000F000F
+    uint32_t bB;   // (64+z, 64+z): bias of pairs taken with mask 0x00F000F0
+};
+
+template <>
+struct ColParams<DT_BF16> {
+    float s;       // the scale, exactly
+    float nzs;     // -z*s, exact in fp32 unless it overflows (then infinite)
+    float zneg;    // -z (used only by the exact form)
+};
+
+__device__ __forceinline__ ColParams<DT_F16> make_params(uint32_t sbits, uint32_t z,
+                                                         ColParams<DT_F16>*) {
+    ColParams<DT_F16> p;
+    p.s2 = sbits * 0x00010001u;
+    p.bA = (0x6400u | z) * 0x00010001u;          // fp16 1024 + z
+    p.bB = (0x5400u | (z << 4)) * 0x00010001u;   // fp16 64 + z (spacing 1/16 at 64)
+    return p;
+}
+
+__device__ __forceinline__ ColParams<DT_BF16> make_params(uint32_t sbits, uint32_t z,
+                                                          ColParams<DT_BF16>*) {
+    ColParams<DT_BF16> p;
+    p.s = __uint_as_float(sbits << 16);
+    p.nzs = -((float)z * p.s);
+    p.zneg = -(float)z;
+    return p;
+}
+
+template <int DT>
+__device__ __forceinline__ ColParams<DT> col_params(uint32_t sbits, uint32_t z) {
+    return make_params(sbits, z, (ColParams<DT>*)nullptr);
+}
+
+// A value the compiler must treat as unknown (kept in a VGPR): stops it from
+// re-deriving bit ranges and picking longer instruction sequences.
+__device__ __forceinline__ uint32_t opaque_v(uint32_t v) {
+    asm("" : "+v"(v));
+    return v;
+}
+
+// (x & m) | g in one VALU instruction.  The backend splits it into v_and +
+// v_or when both constants are literals (gfx9 VOP3 takes no literal and one
+// scalar operand), so it is written out: mask in an SGPR, g in a VGPR.
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t g) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m), "v"(g));
+    return r;
+}
+
+// Eight dequantized weights of one repacked word as the four dwords of an
+// MFMA operand: dword i holds (j = 2i, j = 2i+1) in its (low, high) halves.
+// 13 VALU instructions: 1 shift, 4 v_and_or_b32, 4 v_pk_add_f16, 4 v_pk_mul_f16.
+__device__ __forceinline__ u32x4 dequant_word(uint32_t w, const ColParams<DT_F16>& p) {
+    const uint32_t w8 = w >> 8;
+    const f16x2 s2 = __builtin_bit_cast(f16x2, p.s2);
+    const f16x2 bA = __builtin_bit_cast(f16x2, p.bA);
+    const f16x2 bB = __builtin_bit_cast(f16x2, p.bB);
+    const uint32_t gA = opaque_v(0x64006400u);   // fp16 1024 in both halves
+    const uint32_t gB = opaque_v(0x54005400u);   // fp16 64 in both halves
+    // nibble positions (0,4) -> j (0,1); (1,5) -> (2,3); (2,6) -> (4,5); (3,7) -> (6,7)
+    const f16x2 v0 = __builtin_bit_cast(f16x2, and_or(w, 0x000F000Fu, gA));    // 1024 + q
+    const f16x2 v1 = __builtin_bit_cast(f16x2, and_or(w, 0x00F000F0u, gB));    // 64 + q
+    const f16x2 v2 = __builtin_bit_cast(f16x2, and_or(w8, 0x000F000Fu, gA));
+    const f16x2 v3 = __builtin_bit_cast(f16x2, and_or(w8, 0x00F000F0u, gB));
+    u32x4 r;
+    r.x = __builtin_bit_cast(uint32_t, (f16x2)((v0 - bA) * s2));
+    r.y = __builtin_bit_cast(uint32_t, (f16x2)((v1 - bB) * s2));
+    r.z = __builtin_bit_cast(uint32_t, (f16x2)((v2 - bA) * s2));
+    r.w = __builtin_bit_cast(uint32_t, (f16x2)((v3 - bB) * s2));
+    return r;
+}
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    // one v_cvt_pk_bf16_f32: both values rounded to nearest even
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+}
+
+__device__ __forceinline__ u32x4 dequant_word(uint32_t w, const ColParams<DT_BF16>& p) {
+    // Bytes of lo hold nibble positions 0,2,4,6 (j = 0,4,1,5); bytes of hi hold
+    // positions 1,3,5,7 (j = 2,6,3,7).  Byte -> fp32 is v_cvt_f32_ubyteN.
+    const uint32_t lo = opaque_v(w & 0x0F0F0F0Fu);
+    const uint32_t hi = opaque_v((w >> 4) & 0x0F0F0F0Fu);
+    const float j0 = __builtin_fmaf((float)(lo & 0xFFu), p.s, p.nzs);
+    const float j1 = __builtin_fmaf((float)((lo >> 16) & 0xFFu), p.s, p.nzs);
+    const float j2 = __builtin_fmaf((float)(hi & 0xFFu), p.s, p.nzs);
+    const float j3 = __builtin_fmaf((float)((hi >> 16) & 0xFFu), p.s, p.nzs);
+    const float j4 = __builtin_fmaf((float)((lo >> 8) & 0xFFu), p.s, p.nzs);
+    const float j5 = __builtin_fmaf((float)(lo >> 24), p.s, p.nzs);
+    const float j6 = __builtin_fmaf((float)((hi >> 8) & 0xFFu), p.s, p.nzs);
+    const float j7 = __builtin_fmaf((float)(hi >> 24), p.s, p.nzs);
+    u32x4 r;
+    r.x = pack_bf16x2(j0, j1);
+    r.y = pack_bf16x2(j2, j3);
+    r.z = pack_bf16x2(j4, j5);
+    r.w = pack_bf16x2(j6, j7);
+    return r;
+}
+
+// The fma form above needs -z*s to be exact; it overflows fp32 only for
+// scales beyond fp32_max/15 (about 2.3e37).  For such columns this form is
+// used instead: (q - z) exactly, then one product, then one RNE.
+__device__ __forceinline__ bool needs_exact_path(const ColParams<DT_F16>&) { return false; }
+__device__ __forceinline__ bool needs_exact_path(const ColParams<DT_BF16>& p) {
+    return __builtin_isinf(p.nzs);
+}
+
+__device__ __forceinline__ u32x4 dequant_word_exact(uint32_t w, const ColParams<DT_F16>& p) {
+    return dequant_word(w, p);   // the fp16 form is exact for every scale
+}
+
+__device__ __forceinline__ u32x4 dequant_word_exact(uint32_t w, const ColParams<DT_BF16>& p) {
+    float v[8];
+#pragma unroll
+    for (int p_ = 0; p_ < 8; ++p_) {
+        const int j = 2 * (p_ & 3) + (p_ >> 2);
+        v[j] = ((float)((w >> (4 * p_)) & 0xFu) + p.zneg) * p.s;
+    }
+    u32x4 r;
+    r.x = pack_bf16x2(v[0], v[1]);
+    r.y = pack_bf16x2(v[2], v[3]);
+    r.z = pack_bf16x2(v[4], v[5]);
+    r.w = pack_bf16x2(v[6], v[7]);
+    return r;
+}
+
+template <bool EXACT, int DT>
+__device__ __forceinline__ u32x4 dequant_sel(uint32_t w, const ColParams<DT>& p) {
+    if constexpr (EXACT)
+        return dequant_word_exact(w, p);
+    else
+        return dequant_word(w, p);
+}
+
+// True (for the whole wave) if any lane's column needs the exact form.
+template <int DT>
+__device__ __forceinline__ bool wave_needs_exact(const ColParams<DT> (&prm)[4]) {
+    if constexpr (DT == DT_F16) {
+        return false;
+    } else {
+        const bool b = needs_exact_path(prm[0]) | needs_exact_path(prm[1]) |
+                       needs_exact_path(prm[2]) | needs_exact_path(prm[3]);
+        return __any(b) != 0;
+    }
+}
+
+// Column constants for column tile t (0..3) of a lane, from its scale record
+// entry (four 16-bit scales) and zero record entry (four nibbles).
+template <int DT, bool SYM>
+__device__ __forceinline__ ColParams<DT> tile_params(u32x2 sc, uint32_t zw, int t) {
+    const uint32_t word = (t < 2) ? sc.x : sc.y;
+    const uint32_t sbits = (t & 1) ? (word >> 16) : (word & 0xFFFFu);
+    const uint32_t z = SYM ? 8u : ((zw >> (4 * t)) & 0xFu);
+    return col_params<DT>(sbits, z);
+}
+
+// D = A.B + C on one 32x32x16 tile.  A: lane l holds row l%32, reduction
+// indices 8*(l/32)..+7; B: lane l holds column l%32, the same indices; C/D:
+// lane l, register r holds row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+template <int DT>
+__device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c);
+
+template <>
+__device__ __forceinline__ f32x16 mfma32x32x16<DT_F16>(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+template <>
+__device__ __forceinline__ f32x16 mfma32x32x16<DT_BF16>(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// fp32 -> activation dtype, round to nearest even.
+template <int DT>
+__device__ __forceinline__ uint16_t round_out(float v);
+
+template <>
+__device__ __forceinline__ uint16_t round_out<DT_F16>(float v) {
+    return __builtin_bit_cast(uint16_t, (_Float16)v);
+}
+
+template <>
+__device__ __forceinline__ uint16_t round_out<DT_BF16>(float v) {
+    return __builtin_bit_cast(uint16_t, (__bf16)v);
+}
+
+// Accumulator register r of lane l -> row offset inside a 32x32 tile.
+__device__ __forceinline__ int acc_row(int r, int lane) {
+    return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+}
+
+}  // namespace w4a16

@@ -1,0 +1,43 @@
+// w4a16_internal.h -- launchers and the kernel plan, shared by the C ABI layer
+// and the HIP translation units.  Not part of the public interface.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "w4a16_layout.h"
+
+namespace w4a16 {
+
+enum Variant { VARIANT_SPLITK = 0, VARIANT_TILED = 1 };
+
+// How one w4a16_gemm call is executed.  Computed on the host from the shape
+// only, so w4a16_workspace_bytes and w4a16_gemm always agree.
+struct Plan {
+    Variant variant;
+    int splits;            // S: workgroups that share one output tile along K
+    int steps_per_split;   // k-steps per split (tiled) / per wave (split-K)
+    int mt;                // 32-row MFMA tiles per wave
+    int waves;             // waves per workgroup
+    int grid_x, grid_y, grid_z;
+    int tiles;             // output tiles that own a counter (0 if splits == 1)
+    size_t tile_floats;    // fp32 partial values per (tile, split)
+    size_t counters_bytes; // counter area at the start of the workspace
+    size_t workspace;      // total workspace bytes (0 if splits == 1)
+};
+
+Plan make_plan(int64_t M, int64_t N, int64_t K, int G, uint32_t flags);
+
+// Launchers return the hipError_t of the launch (hipGetLastError()).
+hipError_t launch_repack(const uint32_t* qweight, const void* scales, const uint8_t* zeros,
+                         const Layout& L, bool bf16, void* packed, hipStream_t stream);
+hipError_t launch_unrepack(const void* packed, const Layout& L, bool bf16, uint32_t* qweight,
+                           void* scales, uint8_t* zeros, hipStream_t stream);
+hipError_t launch_dequant(const void* packed, const Layout& L, bool bf16, void* W_out,
+                          hipStream_t stream);
+hipError_t launch_gemm(const void* X, const void* packed, void* Y, int64_t M, const Layout& L,
+                       bool bf16, const Plan& plan, void* workspace, hipStream_t stream);
+hipError_t launch_mfma_probe(const void* A, const void* B, float* D, bool bf16,
+                             hipStream_t stream);
+
+}  // namespace w4a16

@@ -32,8 +32,8 @@ from typing import Optional
 
 import numpy as np
 
-__all__ = ["Problem", "make_problem", "pack_nibbles", "to_dtype_bits", "WORKLOADS",
-           "workload"]
+__all__ = ["Problem", "make_problem", "make_weights", "make_activations", "with_activations",
+           "pack_nibbles", "to_dtype_bits", "WORKLOADS", "workload"]
 
 
 def to_dtype_bits(x64: np.ndarray, dtype: str) -> np.ndarray:
@@ -76,29 +76,51 @@ class Problem:
     q: Optional[np.ndarray] = field(default=None, repr=False)   # uint8 [K][N] if kept
 
 
+def _streams(seed: int):
+    return [np.random.Generator(np.random.PCG64(s))
+            for s in np.random.SeedSequence(seed).spawn(5)]
+
+
+def make_activations(M: int, K: int, dtype: str = "fp16", seed: int = 0,
+                     outlier_frac: float = 0.0, outlier_mult: float = 20.0) -> np.ndarray:
+    """X bit patterns [M][K] (streams 0 and 4 of the seed)."""
+    st = _streams(seed)
+    x64 = st[0].standard_normal((M, K))
+    if outlier_frac > 0:
+        n_out = int(round(outlier_frac * K))
+        if n_out > 0:
+            cols = st[4].choice(K, size=n_out, replace=False)
+            x64[:, cols] *= outlier_mult
+    return to_dtype_bits(x64, dtype)
+
+
+def make_weights(K: int, N: int, G: int = 128, dtype: str = "fp16", sym: bool = False,
+                 seed: int = 0, keep_q: bool = False, scale_range=(0.002, 0.02)):
+    """(qweight, scales, zeros, q or None) (streams 1, 2 and 3 of the seed)."""
+    if K % 8 or K % G:
+        raise ValueError("K must be a multiple of 8 and of G")
+    st = _streams(seed)
+    q = st[1].integers(0, 16, size=(K, N), dtype=np.uint8)
+    qweight = pack_nibbles(q)
+    s64 = st[2].uniform(scale_range[0], scale_range[1], size=(K // G, N))
+    scales = to_dtype_bits(s64, dtype)
+    zeros = None if sym else st[3].integers(0, 16, size=(K // G, N), dtype=np.uint8)
+    return qweight, scales, zeros, (q if keep_q else None)
+
+
 def make_problem(M: int, K: int, N: int, G: int = 128, dtype: str = "fp16",
                  sym: bool = False, seed: int = 0, outlier_frac: float = 0.0,
                  outlier_mult: float = 20.0, keep_q: bool = False,
                  scale_range=(0.002, 0.02)) -> Problem:
-    if K % 8 or K % G:
-        raise ValueError("K must be a multiple of 8 and of G")
-    streams = [np.random.Generator(np.random.PCG64(s))
-               for s in np.random.SeedSequence(seed).spawn(5)]
-    x64 = streams[0].standard_normal((M, K))
-    if outlier_frac > 0:
-        n_out = int(round(outlier_frac * K))
-        if n_out > 0:
-            cols = streams[4].choice(K, size=n_out, replace=False)
-            x64[:, cols] *= outlier_mult
-    X = to_dtype_bits(x64, dtype)
-    del x64
-    q = streams[1].integers(0, 16, size=(K, N), dtype=np.uint8)
-    qweight = pack_nibbles(q)
-    s64 = streams[2].uniform(scale_range[0], scale_range[1], size=(K // G, N))
-    scales = to_dtype_bits(s64, dtype)
-    zeros = None if sym else streams[3].integers(0, 16, size=(K // G, N), dtype=np.uint8)
-    return Problem(M, K, N, G, dtype, bool(sym), X, qweight, scales, zeros,
-                   q if keep_q else None)
+    qweight, scales, zeros, q = make_weights(K, N, G, dtype, sym, seed, keep_q, scale_range)
+    X = make_activations(M, K, dtype, seed, outlier_frac, outlier_mult)
+    return Problem(M, K, N, G, dtype, bool(sym), X, qweight, scales, zeros, q)
+
+
+def with_activations(p: Problem, M: int, seed: int = 0, outlier_frac: float = 0.0) -> Problem:
+    """The same weights as p with a fresh X of M rows."""
+    X = make_activations(M, p.K, p.dtype, seed, outlier_frac)
+    return Problem(M, p.K, p.N, p.G, p.dtype, p.sym, X, p.qweight, p.scales, p.zeros, p.q)
 
 
 # Named workloads (shapes of a 70B-class decoder layer; "outliers" marks the
