@@ -69,9 +69,9 @@ const char *w4a16_status_string(w4a16_status_t status);
 
 /*
  * Size in bytes of the repacked blob for (K, N, G, flags), or 0 if the shape
- * is invalid or unsupported.  It is exactly the algorithmic byte count of the
- * quantized weight: K*N/2 (packed nibbles) + (K/G)*N*2 (scales) +
- * (K/G)*N/2 (zeros, asymmetric only).
+ * is invalid or unsupported: the algorithmic byte count of the quantized
+ * weight, K*N/2 (packed nibbles) + (K/G)*N*2 (scales) + (K/G)*N/2 (zeros,
+ * asymmetric only), plus a 16-byte trailer (format tag and feature flags).
  */
 size_t w4a16_packed_bytes(int64_t K, int64_t N, int group_size, uint32_t flags);
 
@@ -106,7 +106,9 @@ w4a16_status_t w4a16_unrepack(const void *packed, size_t packed_bytes, uint32_t 
 /*
  * Workspace bytes w4a16_gemm needs for this problem (0 = none).  The value
  * depends on the kernel variant and split-K factor chosen for the shape; it is
- * at most 4 KiB + 64 * M_pad * N bytes, M_pad = M rounded up to 32.
+ * at most 64 KiB + 64 * M_pad * N bytes, M_pad = M rounded up to 32.  The
+ * first 64 KiB always hold the per-tile counters, whatever the shape, so one
+ * zero-filled buffer can serve calls of different shapes one after another.
  */
 size_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int group_size, uint32_t flags);
 
@@ -124,12 +126,14 @@ size_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int group_size, ui
  *              use; every call leaves its counters zero again, so one
  *              zero-fill suffices for any number of calls.  Calls that share a
  *              workspace must not run concurrently.
- * Kernel choice: small M uses a split-K streaming kernel whose partial sums
- * are reduced in a fixed order (results are bitwise reproducible run to run);
- * larger M uses an LDS-tiled MFMA kernel.  Both use v_mfma_f32_32x32x16.
- * The environment variables W4A16_FORCE_VARIANT=splitk|tiled and
- * W4A16_SPLITS=<n> override the choice (benchmarking only; they also change
- * w4a16_workspace_bytes).
+ * Kernel choice: M <= 32 uses a split-K streaming kernel (every workgroup
+ * streams an equal share of the weight chunks; partial sums of a split column
+ * block are reduced in a fixed order, so results are bitwise reproducible run
+ * to run); larger M uses an LDS-tiled MFMA kernel.  Both use
+ * v_mfma_f32_32x32x16.  The environment variables
+ * W4A16_FORCE_VARIANT=splitk|tiled, W4A16_SPLITK_WGS=<n> (split-K workgroup
+ * count) and W4A16_SPLITS=<n> (tiled split count) override the choice
+ * (benchmarking only; they also change w4a16_workspace_bytes).
  * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.
  */
 w4a16_status_t w4a16_gemm(const void *X, const void *packed, size_t packed_bytes, void *Y,

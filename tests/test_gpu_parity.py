@@ -157,6 +157,30 @@ def test_gemm_one_hot_rows_are_dequantized_weights(variant, M, K, N, G, dtype, s
     assert same_bits(Y, deq[ks])
 
 
+@pytest.mark.parametrize("variant,M", [("splitk", 3), ("tiled", 70)])
+def test_gemm_exact_bf16_form_for_huge_scales(variant, M):
+    """bf16 scales so large that -z*s overflows fp32 (z = 15, s near 2^125) while
+    every (q - z) * s stays finite (q in {14, 15}): the repack flags the blob and
+    both kernels must still return the dequantized weights bit for bit."""
+    w4 = lib()
+    K, N, G = 256, 256, 64
+    rng = np.random.default_rng(M)
+    q = rng.integers(14, 16, size=(K, N)).astype(np.uint8)
+    scales = rng.integers(0x7E00, 0x7E80, size=(K // G, N)).astype(np.uint16)   # 2^125..2^126
+    zeros = np.full((K // G, N), 15, dtype=np.uint8)
+    X, ks = one_hot_rows(M, K, "bf16")
+    p = synth.Problem(M, K, N, G, "bf16", False, X, synth.pack_nibbles(q), scales, zeros)
+    say(f"exact bf16 form {variant} M={M}")
+    with env(W4A16_FORCE_VARIANT=variant):
+        d = OnDevice(p)
+        flags_word = int(d.packed.data[-8:-4].view(torch.int32).cpu()[0])
+        assert flags_word & 1, "repack did not flag the blob"
+        Y = w4.bits_of(d.gemm())
+    deq = oracle.dequant(p.qweight, p.scales, p.zeros, K, N, G, "bf16", False)
+    assert same_bits(Y, deq[ks])
+    assert same_bits(w4.bits_of(w4.w4a16_dequant(d.packed)), deq)
+
+
 SMALL = [  # (K, N, G, dtype, sym)
     (256, 256, 128, "fp16", False),
     (96, 384, 32, "bf16", True),
@@ -178,13 +202,16 @@ def test_gemm_matches_oracle(M, K, N, G, dtype, sym):
 
 
 @pytest.mark.parametrize("variant,M,splits", [("splitk", 4, 1), ("splitk", 4, 3), ("splitk", 30, 16),
+                                              ("splitk", 1, 7), ("splitk", 9, 100), ("splitk", 2, 5000),
                                               ("tiled", 8, 1), ("tiled", 32, 2), ("tiled", 96, 5),
                                               ("tiled", 200, 16)])
 def test_gemm_forced_variant_and_splits(variant, M, splits):
+    """Forced kernel and work split: for split-K, `splits` is the number of
+    workgroups (1 = one workgroup streams everything; 5000 = more than chunks)."""
     K, N, G = 4096, 640, 64
     p = synth.make_problem(M, K, N, G=G, dtype="bf16", sym=False, seed=M)
     say(f"forced {variant} S={splits} M={M}")
-    with env(W4A16_FORCE_VARIANT=variant, W4A16_SPLITS=splits):
+    with env(W4A16_FORCE_VARIANT=variant, W4A16_SPLITS=splits, W4A16_SPLITK_WGS=splits):
         d = OnDevice(p)
         Y1 = d.gemm()
         Y2 = d.gemm()
@@ -198,9 +225,12 @@ def test_workspace_counters_return_to_zero():
     the counters are zero after each call."""
     w4 = lib()
     ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+    # shapes whose tile counts differ, in an order where a later call has more
+    # tiles than an earlier one wrote partial sums for
     for i, (M, K, N, var) in enumerate([(1, 8192, 1024, "splitk"), (9, 2048, 512, "splitk"),
                                         (40, 4096, 1024, "tiled"), (3, 8192, 1024, "splitk"),
-                                        (70, 8192, 384, "tiled")]):
+                                        (70, 8192, 384, "tiled"), (2, 8192, 4096, "splitk"),
+                                        (1, 4096, 256, "splitk"), (5, 8192, 8192, "splitk")]):
         p = synth.make_problem(M, K, N, G=128, seed=i)
         say(f"workspace reuse call {i}: M={M} K={K} N={N} {var}")
         with env(W4A16_FORCE_VARIANT=var):
@@ -211,10 +241,8 @@ def test_workspace_counters_return_to_zero():
             torch.cuda.synchronize()
         Yref, B = oracle.gemm(p.X, p.qweight, p.scales, p.zeros, M, N, K, 128, "fp16", False)
         assert_gemm_close(p, d.y_float(Y), Yref, B, f"call {i}")
-        # counter area: one uint32 per output tile at the start of the workspace
-        nb = N // 128
-        tiles = nb if var == "splitk" else -(-nb // 4) * -(-M // (32 * (2 if M <= 64 else 4)))
-        assert int(ws[:4 * tiles].count_nonzero()) == 0, "counters not reset"
+        # counter area: the first 64 KiB of every workspace, all zero between calls
+        assert int(ws[:65536].count_nonzero()) == 0, "counters not reset"
 
 
 # ---------------------------------------------------------------------------

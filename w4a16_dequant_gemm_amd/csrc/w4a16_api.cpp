@@ -15,9 +15,13 @@ namespace {
 
 constexpr int kNumCUs = 256;        // MI355X compute units
 constexpr int kMaxSplits = 16;
-constexpr int kSplitKWaves = 8;     // waves per split-K workgroup
-constexpr int kSplitKBatch = 8;     // k-steps per split-K load batch
+constexpr int kSplitKBatch = 8;     // split-K wave ranges are multiples of this many k-steps
 constexpr int kTiledStage = 8;      // k-steps per tiled stage
+// Counter area at the start of every workspace: one uint32 per output tile,
+// at a fixed size for every shape, so the partial sums of one call can never
+// land where another call's counters live when callers share a workspace.
+constexpr size_t kCounterBytes = 64 * 1024;
+constexpr int kMaxTilesSplit = (int)(kCounterBytes / 4);
 constexpr int64_t kMaxDim = (int64_t)1 << 31;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -65,34 +69,29 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int G, uint32_t /*flags*/) {
     (void)G;
 
     if (splitk) {
+        // Stream-K over 8-wave workgroups, one per CU: W workgroups of L
+        // chunks (k-steps of one column block) each.
         p.variant = VARIANT_SPLITK;
         p.mt = 1;
-        p.waves = kSplitKWaves;
-        // Choose the split count S: minimise rounds-of-workgroups x work per
-        // workgroup, with a small charge per split for the partial traffic.
-        int best_s = 1;
-        double best_cost = 1e300;
-        for (int s = 1; s <= kMaxSplits; ++s) {
-            const int64_t spw = round_up(ceil_div(KS, (int64_t)s * kSplitKWaves), kSplitKBatch);
-            const int64_t s_eff = ceil_div(KS, spw * kSplitKWaves);
-            const int64_t wgs = NB * s_eff;
-            const double rounds = (double)ceil_div(wgs, kNumCUs);
-            const double cost = rounds * (double)(spw * kSplitKWaves) + 2.0 * (double)s_eff;
-            if (cost < best_cost - 1e-9) {
-                best_cost = cost;
-                best_s = s;
-            }
-        }
-        if (forced_splits > 0) best_s = forced_splits < kMaxSplits ? forced_splits : kMaxSplits;
-        const int64_t spw = round_up(ceil_div(KS, (int64_t)best_s * kSplitKWaves), kSplitKBatch);
-        p.steps_per_split = (int)spw;
-        p.splits = (int)ceil_div(KS, spw * kSplitKWaves);
-        p.grid_x = (int)NB;
-        p.grid_y = p.splits;
+        p.waves = 8;
+        const int64_t total = NB * KS;
+        // Measured on MI355X: a whole column block per workgroup (no partial
+        // tiles) is fastest once there are enough column blocks to occupy
+        // most CUs; below that, about 128 workgroups share the column blocks.
+        int64_t W = NB >= kNumCUs / 2 ? NB : (kNumCUs / 2);
+        const int forced_wgs = env_int("W4A16_SPLITK_WGS", 0);
+        if (forced_wgs > 0) W = forced_wgs;
+        int64_t Lc = round_up(ceil_div(total, W), kSplitKBatch);
+        if (KS % kSplitKBatch != 0) Lc = round_up(Lc, KS);   // keep segments aligned
+        W = ceil_div(total, Lc);
+        p.steps_per_split = (int)Lc;                           // L
+        p.grid_x = (int)W;
+        p.grid_y = 1;
         p.grid_z = 1;
         p.tiles = (int)NB;
-        const int64_t nq = ceil_div(M, 8);
-        p.tile_floats = (size_t)4 * nq * 64 * 4;
+        p.tile_floats = (size_t)4 * M * 32;                    // one partial slot
+        const bool any_partial = (Lc % KS) != 0;
+        p.splits = any_partial ? (int)(ceil_div(KS, Lc) + 1) : 1;   // max contributors
     } else {
         p.variant = VARIANT_TILED;
         p.mt = M <= 64 ? 2 : 4;
@@ -116,8 +115,20 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int G, uint32_t /*flags*/) {
         p.tiles = (int)tiles;
         p.tile_floats = (size_t)4 * p.mt * 4 * 16 * 64;
     }
+    if (p.variant == VARIANT_TILED && p.splits > 1 && p.tiles > kMaxTilesSplit) {
+        // enough tiles to fill the machine without splitting K
+        p.splits = 1;
+        p.steps_per_split = (int)round_up(KS, kTiledStage);
+        p.grid_z = 1;
+    }
+    if (p.variant == VARIANT_SPLITK && p.splits > 1 && p.tiles > kMaxTilesSplit) {
+        // too many column blocks for the counter area: whole column blocks per wave
+        p.steps_per_split = (int)round_up(p.steps_per_split, KS);
+        p.grid_x = (int)ceil_div(NB * KS, p.steps_per_split);
+        p.splits = 1;
+    }
     if (p.splits > 1) {
-        p.counters_bytes = (size_t)round_up((int64_t)p.tiles * 4, 256);
+        p.counters_bytes = kCounterBytes;
         p.workspace = p.counters_bytes + (size_t)p.tiles * p.splits * p.tile_floats * 4;
     } else {
         p.tiles = 0;

@@ -20,8 +20,8 @@
 //         through fp32: fma(q, s, -z*s) is exact (|q - z| <= 15 has 4 bits, s
 //         has 8 significant bits, and -z*s is itself exact), then
 //         v_cvt_pk_bf16_f32 rounds once per value.  When -z*s overflows fp32
-//         (scales above about 2.3e37) a wave switches to (q - z) * s, also
-//         exact before the one rounding.
+//         (scales above about 2.3e37) the launch uses (q - z) * s instead,
+//         also exact before the one rounding (a flag in the blob trailer).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -180,18 +180,6 @@ __device__ __forceinline__ u32x4 dequant_sel(uint32_t w, const ColParams<DT>& p)
         return dequant_word_exact(w, p);
     else
         return dequant_word(w, p);
-}
-
-// True (for the whole wave) if any lane's column needs the exact form.
-template <int DT>
-__device__ __forceinline__ bool wave_needs_exact(const ColParams<DT> (&prm)[4]) {
-    if constexpr (DT == DT_F16) {
-        return false;
-    } else {
-        const bool b = needs_exact_path(prm[0]) | needs_exact_path(prm[1]) |
-                       needs_exact_path(prm[2]) | needs_exact_path(prm[3]);
-        return __any(b) != 0;
-    }
 }
 
 // Column constants for column tile t (0..3) of a lane, from its scale record

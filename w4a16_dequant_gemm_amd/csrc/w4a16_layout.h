@@ -29,6 +29,12 @@
 // Region Z (asymmetric only; offset K*N/2 + NG*N*2, NG*N/2 bytes): one 64-byte
 // record per (nb, g).  The 16-bit entry at 2*c32 holds, in nibble t, the zero
 // point of column 128*nb + 32*t + c32 for group g.
+//
+// Trailer (16 bytes, after region Z): uint32 magic kTrailerMagic, uint32 layout
+// version, uint32 feature flags, uint32 group size.  Feature flag
+// kFlagExactBf16 is set by the repack when some column's -z*s overflows fp32
+// (bf16 scales above about 2.3e37); the GEMM kernels then use the exact
+// dequant form for the whole launch instead of testing every group.
 #pragma once
 #include <stddef.h>
 #include <stdint.h>
@@ -40,12 +46,15 @@ constexpr int kKStep = 16;         // reduction indices per k-step
 constexpr int kChunkBytes = 1024;  // one (column block, k-step) chunk
 constexpr int kScaleRecBytes = 256;
 constexpr int kZeroRecBytes = 64;
+constexpr int kTrailerBytes = 16;
+constexpr uint32_t kTrailerMagic = 0x36314134u;   // "4A16"
+constexpr uint32_t kFlagExactBf16 = 1u;
 
 struct Layout {
     int64_t K, N, G;
     bool sym;
     int64_t NB, KS, NG;
-    size_t w_bytes, s_off, s_bytes, z_off, z_bytes, total;
+    size_t w_bytes, s_off, s_bytes, z_off, z_bytes, t_off, total;
 };
 
 inline Layout make_layout(int64_t K, int64_t N, int64_t G, bool sym) {
@@ -62,7 +71,8 @@ inline Layout make_layout(int64_t K, int64_t N, int64_t G, bool sym) {
     L.s_bytes = (size_t)L.NG * (size_t)N * 2;
     L.z_off = L.s_off + L.s_bytes;
     L.z_bytes = sym ? 0 : (size_t)L.NG * (size_t)N / 2;
-    L.total = L.z_off + L.z_bytes;
+    L.t_off = L.z_off + L.z_bytes;
+    L.total = L.t_off + kTrailerBytes;
     return L;
 }
 

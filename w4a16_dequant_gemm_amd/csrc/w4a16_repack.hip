@@ -71,11 +71,19 @@ __global__ void unrepack_words_kernel(const uint32_t* __restrict__ in,
     qweight[p.row * N + p.col] = repacked_to_canonical(in[idx]);
 }
 
-// One thread per (nb, g, c32): four scales and four zeros.
+__global__ void init_trailer_kernel(uint32_t* __restrict__ trailer, uint32_t group_size) {
+    trailer[0] = kTrailerMagic;
+    trailer[1] = 1u;   // layout version
+    trailer[2] = 0u;   // feature flags, OR-ed by repack_meta_kernel
+    trailer[3] = group_size;
+}
+
+// One thread per (nb, g, c32): four scales and four zeros.  For bf16 it also
+// flags the blob when -z*s overflows fp32 for some column.
 __global__ void repack_meta_kernel(const uint16_t* __restrict__ scales,
                                    const uint8_t* __restrict__ zeros, uint8_t* __restrict__ packed,
                                    int64_t N, int64_t NG, size_t s_off, size_t z_off,
-                                   int64_t nrec32) {
+                                   size_t t_off, int bf16, int64_t nrec32) {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= nrec32) return;
     const int c32 = (int)(idx & 31);
@@ -84,13 +92,18 @@ __global__ void repack_meta_kernel(const uint16_t* __restrict__ scales,
     const int64_t nb = rec / NG;
     uint16_t* srec = (uint16_t*)(packed + s_off + rec * kScaleRecBytes) + 4 * c32;
     uint32_t zword = 0;
+    bool needs_exact = false;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const int64_t col = nb * kColBlock + 32 * t + c32;
-        srec[t] = scales[g * N + col];
-        if (zeros) zword |= (uint32_t)(zeros[g * N + col] & 0xFu) << (4 * t);
+        const uint16_t sb = scales[g * N + col];
+        const uint32_t z = zeros ? (uint32_t)(zeros[g * N + col] & 0xFu) : 8u;
+        srec[t] = sb;
+        zword |= z << (4 * t);
+        if (bf16) needs_exact |= needs_exact_path(col_params<DT_BF16>(sb, z));
     }
     if (zeros) ((uint16_t*)(packed + z_off + rec * kZeroRecBytes))[c32] = (uint16_t)zword;
+    if (needs_exact) atomicOr((uint32_t*)(packed + t_off) + 2, kFlagExactBf16);
 }
 
 __global__ void unrepack_meta_kernel(const uint8_t* __restrict__ packed,
@@ -149,14 +162,16 @@ inline unsigned blocks_for(int64_t n, int threads) { return (unsigned)((n + thre
 }  // namespace
 
 hipError_t launch_repack(const uint32_t* qweight, const void* scales, const uint8_t* zeros,
-                         const Layout& L, bool /*bf16*/, void* packed, hipStream_t stream) {
+                         const Layout& L, bool bf16, void* packed, hipStream_t stream) {
     const int64_t nwords = (int64_t)(L.w_bytes / 4);
     const int64_t nrec32 = L.NB * L.NG * 32;
     hipLaunchKernelGGL(repack_words_kernel, dim3(blocks_for(nwords, 256)), dim3(256), 0, stream,
                        qweight, (uint32_t*)packed, L.N, L.KS, nwords);
+    hipLaunchKernelGGL(init_trailer_kernel, dim3(1), dim3(1), 0, stream,
+                       (uint32_t*)((uint8_t*)packed + L.t_off), (uint32_t)L.G);
     hipLaunchKernelGGL(repack_meta_kernel, dim3(blocks_for(nrec32, 256)), dim3(256), 0, stream,
                        (const uint16_t*)scales, L.sym ? nullptr : zeros, (uint8_t*)packed, L.N,
-                       L.NG, L.s_off, L.z_off, nrec32);
+                       L.NG, L.s_off, L.z_off, L.t_off, bf16 ? 1 : 0, nrec32);
     return hipGetLastError();
 }
 
