@@ -96,15 +96,15 @@ def gemm(lib, X=FAKE, packed=FAKE, pbytes=1 << 40, Y=FAKE, M=8, N=4096, K=4096, 
     (dict(Y=FAKE_MIS), w4.W4A16_ERR_INVALID_ARG),
     (dict(packed=FAKE_MIS), w4.W4A16_ERR_INVALID_ARG),
     (dict(pbytes=100), w4.W4A16_ERR_INVALID_ARG),        # blob too small
-    (dict(M=8, K=8192, N=28672, ws=NULL), w4.W4A16_ERR_WORKSPACE),
-    (dict(M=8, K=8192, N=28672, wsb=16), w4.W4A16_ERR_WORKSPACE),
-    (dict(M=8, K=8192, N=28672, ws=FAKE_MIS), w4.W4A16_ERR_WORKSPACE),
+    (dict(M=8, K=8192, N=4096, ws=NULL), w4.W4A16_ERR_WORKSPACE),
+    (dict(M=8, K=8192, N=4096, wsb=16), w4.W4A16_ERR_WORKSPACE),
+    (dict(M=8, K=8192, N=4096, ws=FAKE_MIS), w4.W4A16_ERR_WORKSPACE),
     (dict(M=1 << 31), w4.W4A16_ERR_INVALID_ARG),
 ])
 def test_gemm_rejects_before_any_launch(lib, kw, expect):
     if kw.get("ws", FAKE) is not FAKE or kw.get("wsb", 1) == 16:
         # these need a plan that uses a workspace
-        assert w4.w4a16_workspace_bytes(8, 28672, 8192, 128, 0) > 0
+        assert w4.w4a16_workspace_bytes(8, 4096, 8192, 128, 0) > 0
     assert gemm(lib, **kw) == expect
 
 
