@@ -72,7 +72,11 @@ def cpu_baseline(name, cfg, budget_s=12.0):
     probe = min(N, max(threads, 64))
     t_probe = run(probe)
     ncol = int(min(N, max(probe, probe * budget_s / max(t_probe, 1e-6))))
-    t = run(ncol) if ncol > probe else t_probe
+    # repeat the sample until about budget_s of CPU time has been spent
+    times = [run(ncol)]
+    while sum(times) < budget_s and len(times) < 64:
+        times.append(run(ncol))
+    t = float(np.mean(times))
     t_full = t * (N / ncol) * (M / rows)
     return {
         "value": round(algorithmic_bytes(cfg) / t_full / 1e9, 4),
@@ -80,9 +84,37 @@ def cpu_baseline(name, cfg, budget_s=12.0):
         "cores": threads,
         "kind": "oracle",
         "sample": f"{rows} of {M} rows x {ncol} of {N} columns (K={K}) of the same workload, "
-                  f"{t:.1f} s on {threads} threads, rate extrapolated linearly to the full "
-                  f"{M}x{N} output ({t_full:.1f} s)",
+                  f"{len(times)} runs, {t:.2f} s each on {threads} threads (the C oracle: "
+                  f"per-element dequant with its own RNE, fp64 dot products); rate "
+                  f"extrapolated linearly to the full {M}x{N} output ({t_full:.2f} s)",
     }
+
+
+KERNEL_SOURCES = ("w4a16_gemm.hip", "w4a16_device.h", "w4a16_layout.h", "w4a16_api.cpp")
+
+
+def kernel_source_hash():
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "w4a16_dequant_gemm_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(name):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    record of this workload, or None if there is none or the kernel sources
+    changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh).get(name)
+    if not rec or rec.get("source_hash") != kernel_source_hash():
+        return None
+    return int(rec["traffic_bytes"])
 
 
 def run_workload(name, steps, warmup, rotate_bytes=1 << 30, with_cpu=True, comparators=True):
@@ -134,11 +166,13 @@ def run_workload(name, steps, warmup, rotate_bytes=1 << 30, with_cpu=True, compa
     if bound == "hbm":
         achieved = nbytes / (kern_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(name)}
     else:
         achieved = flops / (kern_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_TFLOPS, 4), "traffic": None}
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_TFLOPS, 4),
+                "traffic": measured_traffic(name)}
     out = {
         "metric": METRIC,
         "value": round(nbytes / (ms_step * 1e-3) / 1e9, 1),
@@ -160,6 +194,8 @@ def run_workload(name, steps, warmup, rotate_bytes=1 << 30, with_cpu=True, compa
         "kernel_us_p10_p50_p90": [round(float(np.percentile(per_launch, q)) * 1e3, 3)
                                   for q in (10, 50, 90)],
         "tflops": round(flops / (kern_ms * 1e-3) / 1e12, 2),
+        "algorithmic_bytes": nbytes,
+        "kernel_source_hash": kernel_source_hash(),
         "weight_only_gbs": round((p.K * p.N // 2) / (kern_ms * 1e-3) / 1e9, 1),
         "roofline": roof,
     }
@@ -215,12 +251,23 @@ def main():
                     help="a name from w4a16_synth.WORKLOADS, or 'all' (one line each)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-comparators", action="store_true")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="before the workload, run a plain device copy of this many MiB (a "
+                         "known-size kernel for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; the W4A16 path "
                                    "has no multi-GPU mode (see the sharding notes in DESIGN.md)",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
+    if args.calibration_copy_mib > 0:
+        import torch
+        src = torch.ones(args.calibration_copy_mib << 20, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     names = list(synth.WORKLOADS) if args.workload == "all" else [args.workload]
     for name in names:
         out = run_workload(name, args.steps, args.warmup,
