@@ -106,9 +106,10 @@ w4a16_status_t w4a16_unrepack(const void *packed, size_t packed_bytes, uint32_t 
 /*
  * Workspace bytes w4a16_gemm needs for this problem (0 = none).  The value
  * depends on the kernel variant and split-K factor chosen for the shape; it is
- * at most 64 KiB + 64 * M_pad * N bytes, M_pad = M rounded up to 32.  The
- * first 64 KiB always hold the per-tile counters, whatever the shape, so one
- * zero-filled buffer can serve calls of different shapes one after another.
+ * at most 64 KiB + max(64 * M_pad * N, 262144 * M) bytes, M_pad = M rounded
+ * up to 32.  The first 64 KiB always hold the per-tile counters, whatever the
+ * shape, so one zero-filled buffer can serve calls of different shapes one
+ * after another.
  */
 size_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int group_size, uint32_t flags);
 
@@ -126,10 +127,10 @@ size_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int group_size, ui
  *              use; every call leaves its counters zero again, so one
  *              zero-fill suffices for any number of calls.  Calls that share a
  *              workspace must not run concurrently.
- * Kernel choice: M <= 32 uses a split-K streaming kernel (every workgroup
- * streams an equal share of the weight chunks; partial sums of a split column
- * block are reduced in a fixed order, so results are bitwise reproducible run
- * to run); larger M uses an LDS-tiled MFMA kernel.  Both use
+ * Kernel choice: M <= 32 uses a split-K streaming kernel (every wave streams
+ * an equal contiguous share of the weight chunks; partial sums of a split
+ * column block are reduced in a fixed order, so results are bitwise
+ * reproducible run to run); larger M uses an LDS-tiled MFMA kernel.  Both use
  * v_mfma_f32_32x32x16.  The environment variables
  * W4A16_FORCE_VARIANT=splitk|tiled, W4A16_SPLITK_WGS=<n> (split-K workgroup
  * count) and W4A16_SPLITS=<n> (tiled split count) override the choice

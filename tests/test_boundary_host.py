@@ -66,10 +66,12 @@ def test_packed_bytes_is_the_algorithmic_weight_bytes_plus_trailer(lib, K, N, G,
 def test_workspace_bytes(lib):
     assert w4.w4a16_workspace_bytes(0, 4096, 4096, 128, 0) == 0
     assert w4.w4a16_workspace_bytes(1, 4096, 4096, 128, 0x8) == 0
-    for M in (1, 8, 32, 33, 128, 4096):
-        ws = w4.w4a16_workspace_bytes(M, 28672, 8192, 128, 0)
+    for M, N, K in [(1, 28672, 8192), (8, 28672, 8192), (32, 28672, 8192), (33, 28672, 8192),
+                    (128, 28672, 8192), (4096, 28672, 8192), (2, 128, 1 << 20), (32, 128, 1 << 20),
+                    (1, 4096, 4096), (16, 8192, 28672)]:
+        ws = w4.w4a16_workspace_bytes(M, N, K, 128, 0)
         Mp = -(-M // 32) * 32
-        assert 0 <= ws <= 64 * Mp * 28672 + 65536
+        assert 0 <= ws <= max(64 * Mp * N, 262144 * M) + 65536
         assert ws == 0 or ws > 65536
 
 

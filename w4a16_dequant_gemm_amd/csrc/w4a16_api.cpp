@@ -15,7 +15,6 @@ namespace {
 
 constexpr int kNumCUs = 256;        // MI355X compute units
 constexpr int kMaxSplits = 16;
-constexpr int kSplitKBatch = 8;     // split-K wave ranges are multiples of this many k-steps
 constexpr int kTiledStage = 8;      // k-steps per tiled stage
 // Counter area at the start of every workspace: one uint32 per output tile,
 // at a fixed size for every shape, so the partial sums of one call can never
@@ -69,29 +68,46 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int G, uint32_t /*flags*/) {
     (void)G;
 
     if (splitk) {
-        // Stream-K over 8-wave workgroups, one per CU: W workgroups of L
-        // chunks (k-steps of one column block) each.
+        // Balanced contiguous ranges of batches for every wave of one
+        // workgroup per CU (fewer workgroups when there are fewer batches).
         p.variant = VARIANT_SPLITK;
         p.mt = 1;
-        p.waves = 8;
-        const int64_t total = NB * KS;
-        // Measured on MI355X: a whole column block per workgroup (no partial
-        // tiles) is fastest once there are enough column blocks to occupy
-        // most CUs; below that, about 128 workgroups share the column blocks.
-        int64_t W = NB >= kNumCUs / 2 ? NB : (kNumCUs / 2);
+        p.waves = kSplitKWaves;
+        p.nbat = (int)ceil_div(KS, kSplitKBatch);
+        const int64_t TB = NB * p.nbat;
+        // Measured on MI355X: whole column blocks per workgroup (no partial
+        // tiles shared between workgroups) when that still occupies at least
+        // 3/4 of the CUs; otherwise one workgroup per CU, but at least two
+        // batches per wave (small problems pay more for shared tiles than
+        // they gain from more CUs).
+        const int64_t per_wg = ceil_div(NB, kNumCUs);          // blocks per workgroup
+        int64_t W = ceil_div(NB, per_wg);
+        if (W * 4 < kNumCUs * 3) W = kNumCUs;
+        if (W > TB / (2 * p.waves)) W = TB / (2 * p.waves);
+        if (W < 1) W = 1;
         const int forced_wgs = env_int("W4A16_SPLITK_WGS", 0);
         if (forced_wgs > 0) W = forced_wgs;
-        int64_t Lc = round_up(ceil_div(total, W), kSplitKBatch);
-        if (KS % kSplitKBatch != 0) Lc = round_up(Lc, KS);   // keep segments aligned
-        W = ceil_div(total, Lc);
-        p.steps_per_split = (int)Lc;                           // L
+        if (W > ceil_div(TB, p.waves)) W = ceil_div(TB, p.waves);   // every workgroup has work
+        if (W > kMaxTilesSplit) W = kMaxTilesSplit;                  // counters fit their area
+        const int64_t TW = W * p.waves;
+        p.base = (int)(TB / TW);
+        p.rem = (int)(TB % TW);
         p.grid_x = (int)W;
         p.grid_y = 1;
         p.grid_z = 1;
-        p.tiles = (int)NB;
-        p.tile_floats = (size_t)4 * M * 32;                    // one partial slot
-        const bool any_partial = (Lc % KS) != 0;
-        p.splits = any_partial ? (int)(ceil_div(KS, Lc) + 1) : 1;   // max contributors
+        // A column block is shared by workgroups when a workgroup boundary
+        // falls inside it; each workgroup then has at most two partial tiles
+        // (its first and its last column block) and the counter of a shared
+        // block is indexed by the first workgroup that touches it.
+        bool shared = false;
+        for (int64_t g = 1; g < W && !shared; ++g) {
+            const int64_t gw = g * p.waves;
+            const int64_t b = gw * p.base + (gw < p.rem ? gw : p.rem);
+            shared = b % p.nbat != 0;
+        }
+        p.tiles = (int)W;
+        p.tile_floats = (size_t)4 * M * 32;
+        p.splits = shared ? 2 : 1;                              // partial tiles per workgroup
     } else {
         p.variant = VARIANT_TILED;
         p.mt = M <= 64 ? 2 : 4;
@@ -120,12 +136,6 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int G, uint32_t /*flags*/) {
         p.splits = 1;
         p.steps_per_split = (int)round_up(KS, kTiledStage);
         p.grid_z = 1;
-    }
-    if (p.variant == VARIANT_SPLITK && p.splits > 1 && p.tiles > kMaxTilesSplit) {
-        // too many column blocks for the counter area: whole column blocks per wave
-        p.steps_per_split = (int)round_up(p.steps_per_split, KS);
-        p.grid_x = (int)ceil_div(NB * KS, p.steps_per_split);
-        p.splits = 1;
     }
     if (p.splits > 1) {
         p.counters_bytes = kCounterBytes;

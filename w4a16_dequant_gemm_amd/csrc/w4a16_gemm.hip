@@ -10,16 +10,17 @@
 // Two variants (page "W4A16 GEMM 算子浅析", section "硬件性能拐点": small
 // batches are bound by memory bandwidth, large batches by the matrix units):
 //
-//  * splitk_kernel (M <= 32).  Memory-bound streaming.  A workgroup owns one
-//    128-column block and a slice of K; its 8 waves split that slice further.
-//    Each lane issues one 16-byte load per k-step (the whole 1 KiB chunk per
-//    wave), eight k-steps per batch, two batches in flight.  The activation
-//    rows come straight from global memory (they are tiny and L2-resident).
-//    Partial sums are reduced across waves through LDS and across workgroups
-//    through a workspace, both in a fixed order.  The multiply-accumulate
-//    runs on v_mfma_f32_32x32x16 even at M = 1: the vector ALUs are the
-//    scarce resource on MI355X at this bandwidth (they carry the unpack and
-//    dequant), while the matrix units are idle.
+//  * splitk_kernel (M <= 32).  Memory-bound streaming.  The weight chunks
+//    (one 1 KiB chunk per k-step of a 128-column block) are dealt out in equal
+//    contiguous ranges to every wave of the grid; each lane issues one
+//    16-byte load per k-step, and each wave keeps two 4-k-step batches in
+//    flight while it computes a third.  The activation rows come straight
+//    from global memory (they are tiny and L2-resident).  Partial sums of a
+//    column block split between waves are reduced through LDS and between
+//    workgroups through a workspace, both in a fixed order.  The
+//    multiply-accumulate runs on v_mfma_f32_32x32x16 even at M = 1: the
+//    vector ALUs are the scarce resource on MI355X at this bandwidth (they
+//    carry the unpack and dequant), while the matrix units are idle.
 //
 //  * tiled_kernel (M > 32).  A workgroup of 4 waves owns 32*MT rows by 512
 //    columns; each wave owns one 128-column block, dequantizes each weight
@@ -43,12 +44,6 @@ namespace w4a16 {
 
 namespace {
 
-
-// k-steps per split-K load batch.  Two waves share a SIMD, so each has 256
-// registers including the 64 accumulators; the bf16 dequant (eight fp32
-// temporaries per word) needs the smaller batch to stay out of scratch.
-template <int DT>
-constexpr int splitk_batch() { return DT == DT_BF16 ? 4 : 8; }
 
 __device__ __forceinline__ u32x4 load_weights(const u32x4* p) {
     return __builtin_nontemporal_load(p);   // streamed once: do not keep in cache
@@ -103,280 +98,325 @@ __device__ __forceinline__ void reset_counter(uint32_t* counter) {
 }
 
 // ---------------------------------------------------------------------------
-// Split-K streaming kernel, M <= 32 ("stream-K" over workgroups).
+// Split-K streaming kernel, M <= 32.
 //
-// The weight chunks are numbered c = nb*KS + ks (column block major).
-// Workgroup g (8 waves, one per CU) owns the contiguous range [g*L, (g+1)*L):
-// every workgroup streams the same number of bytes and all of them run in one
-// round.  The range crosses column blocks, so the workgroup works through one
-// or more segments (nb, [kb, ke)).
+// The weight chunks (one 1 KiB chunk = one k-step of one 128-column block)
+// are grouped in batches of SK_U k-steps inside a column block; batch
+// B = nb * nbat + i covers k-steps [i*SK_U, min(KS, (i+1)*SK_U)) of column
+// block nb.  The TB = NB * nbat batches are dealt out in balanced contiguous
+// ranges to every wave of the grid (one workgroup of SK_WAVES waves per CU,
+// two waves per SIMD so that one wave's dequantization overlaps the other's
+// matrix instructions).  A wave streams its range as one continuous
+// pipeline: while it computes batch b, batches b+1 and b+2 (weights, their
+// scale/zero records and the activation operands) are in flight in
+// registers, across column-block boundaries.  No barrier and no LDS traffic
+// in the main loop.
 //
-// Inside a segment the workgroup advances in super-batches of 8 batches: wave
-// w computes batch w of each super-batch.  Each wave keeps its next NBUF-1
-// batches of weights in flight in registers (the HBM stream), while the
-// activation rows of the super-batch are staged once through LDS (double
-// buffered, one barrier per super-batch) instead of occupying registers: they
-// carry no HBM traffic and would otherwise take half of each batch's
-// registers.  At the segment's end the waves reduce their partial tiles
-// through LDS in a fixed order, and then
-//   * a segment that covers a whole column block writes Y;
-//   * otherwise the workgroup stores its partial tile (rows < M only) in slot
-//     (nb, g - first workgroup of nb) and bumps nb's counter; the workgroup
-//     that arrives last adds the column block's slots in workgroup order
-//     (bitwise reproducible) and writes Y.
-// L and KS are multiples of 8 k-steps (or L is a multiple of KS), so every
-// segment starts on a batch and group boundary.
+// Where the range leaves a column block, a block the wave covered entirely
+// is written to Y; the wave's first block, if partial, goes to the wave's LDS
+// slot (its "head"); the last segment of the range stays in the accumulators
+// (its "tail") and is written to Y at once if it is a whole block.  At the end
+// the workgroup handles its partial blocks in increasing order: waves whose
+// tail is that block copy it to their slot (free by then), and the slots are
+// added in wave order.  A block inside the workgroup's range goes to Y; a block
+// shared with other workgroups goes through the workspace: a partial tile per
+// workgroup, a counter per block, and the last arrival adds the partial tiles
+// in workgroup order (bitwise reproducible) and writes Y.
 // ---------------------------------------------------------------------------
-constexpr int SK_WAVES = 8;
+constexpr int SK_WAVES = kSplitKWaves;
+constexpr int SK_U = kSplitKBatch;
+constexpr int SK_NBUF = 3;   // batches held in registers per wave
 
-template <int DT>
-constexpr int splitk_nbuf() { return DT == DT_BF16 ? 4 : 3; }   // weight batches per wave
-
-template <int DT>
-constexpr int splitk_xpitch() {   // LDS row pitch of a staged activation tile, halves
-    return SK_WAVES * splitk_batch<DT>() * kKStep + 8;   // +16 B against bank conflicts
+// Balanced contiguous split of TB batches over the grid's waves: wave gw
+// starts at gw*base + min(gw, rem) and owns base (+1 if gw < rem) batches.
+__device__ __forceinline__ int range_start(int gw, int base, int rem) {
+    return gw * base + min(gw, rem);
+}
+__device__ __forceinline__ int wave_of_batch(int b, int base, int rem) {
+    const int big = rem * (base + 1);
+    return b < big ? b / (base + 1) : rem + (b - big) / base;
 }
 
-template <int DT, int MB>
-constexpr int splitk_lds_bytes() {
-    const int xs = 2 * MB * splitk_xpitch<DT>() * 2;
-    const int red = (SK_WAVES / 2) * 4 * 4 * 64 * 16;
-    return xs > red ? xs : red;
+// The partial column blocks of the wave range [s, e): the head (first block,
+// written to the LDS slot in the main loop) and the tail (last segment, left
+// in the accumulators); -1 if none.
+struct WaveParts {
+    int head, tail;
+};
+__device__ __forceinline__ WaveParts wave_parts(int s, int e, int nbat) {
+    WaveParts w{-1, -1};
+    if (s >= e) return w;
+    const int hb = s / nbat, tb = (e - 1) / nbat;
+    if (hb != tb && s % nbat != 0) w.head = hb;
+    if (!(e % nbat == 0 && (tb != hb || s % nbat == 0))) w.tail = tb;
+    return w;
 }
 
-// MB: rows of the activation tile (8, 16 or 32 >= M), sizes the staging.
+// MB: 8, 16 or 32 >= M (sizes the LDS slots).
 template <int DT, bool SYM, int GS, int MB>
 __global__ __launch_bounds__(SK_WAVES * 64) void splitk_kernel(
     const uint16_t* __restrict__ X, const uint8_t* __restrict__ packed, uint16_t* __restrict__ Y,
-    float* __restrict__ part, uint32_t* __restrict__ cnt, int M, int N, int K, int L, int maxc,
-    size_t s_off, size_t z_off, size_t t_off) {
-    constexpr int SK_U = splitk_batch<DT>();
-    constexpr int NBUF = splitk_nbuf<DT>();
-    constexpr int SB = SK_WAVES * SK_U;          // k-steps per super-batch
-    constexpr int XP = splitk_xpitch<DT>();      // LDS row pitch (halves)
-    constexpr int XCPR = SB * 2;                 // 16-byte activation chunks per row
+    float* __restrict__ part, uint32_t* __restrict__ cnt, int M, int N, int K, int nbat, int base,
+    int rem, size_t s_off, size_t z_off, size_t t_off) {
     constexpr int SPG = GS < SK_U ? GS : SK_U;   // k-steps per group inside a batch
     constexpr int NGB = SK_U / SPG;              // groups (or group parts) per batch
-    constexpr int XCH = MB * XCPR / (SK_WAVES * 64);   // activation chunks per thread
-    static_assert(XCH >= 1 && MB * XCPR == XCH * SK_WAVES * 64, "tile split");
+    constexpr int QMAX = MB / 8;                 // 8-row accumulator groups that can hold rows < M
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int wg = blockIdx.x;
     const int KS = K / kKStep;
-    const int NB = N / kColBlock;
     const int NG = K / (kKStep * GS);
-    const int64_t total = (int64_t)NB * KS;
-    const int64_t c0 = (int64_t)wg * L;
-    const int64_t c1 = min(c0 + (int64_t)L, total);
-    if (c0 >= c1) return;
+    const int QM = (M + 7) >> 3;
+    const int gw = wg * SK_WAVES + wave;
+    const int s_w = range_start(gw, base, rem);
+    const int len = base + (gw < rem ? 1 : 0);
 
-    __shared__ __align__(16) uint8_t lds[splitk_lds_bytes<DT, MB>()];
+    __shared__ f32x4 slots[SK_WAVES][4][QMAX][64];   // [wave][t][q][lane]
     __shared__ uint32_t s_last;
-    uint16_t* xs = (uint16_t*)lds;                 // [2][MB rows][XP], during the main loop
-    f32x4(*red)[4][4][64] = (f32x4(*)[4][4][64])lds;   // [4][t][q][lane], after it
+    __shared__ int s_prog[SK_WAVES];                 // batches computed, per wave
+    __shared__ WaveParts s_parts[SK_WAVES];
 
     const bool exact = uses_exact_form<DT>(packed, t_off);
-    const int lrow = 4 * (lane >> 5);   // accumulator register r: row 8*(r/4) + r%4 + lrow
-    const int lcol = lane & 31;
     // A operand of this lane: activation row min(lane%32, M-1) (rows >= M only
-    // feed output rows that are never stored), 8 halves at 8*(lane/32).
+    // feed accumulator rows that are never stored), 8 halves at 8*(lane/32).
     const int arow = min(lane & 31, M - 1);
+    const uint16_t* xlane = X + (size_t)arow * K + 8 * (lane >> 5);
+    const uint8_t* srec = packed + s_off + (lane & 31) * 8;
+    const uint8_t* zrec = packed + z_off + (lane & 31) * 2;
 
     struct Batch {
+        u32x4 w[SK_U];
+        u32x4 x[SK_U];
         u32x2 sc[NGB];
         uint32_t zw[NGB];
-        u32x4 w[SK_U];
+    };
+
+    // Loads of one batch, all unconditional so that the compiler can count
+    // exactly how many are still in flight.  Past the end of the range they
+    // read cache-resident data instead (the lane's activations and the first
+    // scale/zero record; values never used), so that the final wait for
+    // outstanding loads does not wait for HBM.
+    const int hb = s_w / nbat, ib = s_w - hb * nbat;   // first batch: block, batch in block
+    int nbL = hb, iL = ib, issued = 0;
+    auto issue = [&](Batch& b) {
+        const bool real = issued < len;
+        const int ks0 = real ? iL * SK_U : 0;
+        const int nv = real ? min(SK_U, KS - ks0) : 1;
+        const size_t chunk0 = real ? (size_t)nbL * KS + ks0 : 0;
+        const size_t rec0 = real ? (size_t)nbL * NG + ks0 / GS : 0;
+#pragma unroll
+        for (int q = 0; q < NGB; ++q) {
+            const size_t rec = rec0 + (size_t)min(q * SPG, nv - 1) / GS;
+            b.sc[q] = *(const u32x2*)(srec + rec * kScaleRecBytes);
+            b.zw[q] = SYM ? 0u : (uint32_t)*(const uint16_t*)(zrec + rec * kZeroRecBytes);
+        }
+        const u32x4* wsrc = real ? (const u32x4*)packed + chunk0 * 64 + lane : (const u32x4*)xlane;
+        const int wstep = real ? 64 : 0;
+#pragma unroll
+        for (int u = 0; u < SK_U; ++u) {
+            const int uu = min(u, nv - 1);
+            b.w[u] = load_weights(wsrc + uu * wstep);
+            b.x[u] = *(const u32x4*)(xlane + (size_t)(ks0 + uu) * kKStep);
+        }
+        ++issued;
+        if (++iL == nbat) {
+            iL = 0;
+            ++nbL;
+        }
     };
 
     f32x16 acc[4];
-    const int nb_first = (int)(c0 / KS);
-    const int nb_last = (int)((c1 - 1) / KS);
-    for (int nb = nb_first; nb <= nb_last; ++nb) {
-        const int kb = (int)(max(c0, (int64_t)nb * KS) - (int64_t)nb * KS);
-        const int ke = (int)(min(c1, (int64_t)(nb + 1) * KS) - (int64_t)nb * KS);
-        const int nsb = (ke - kb + SB - 1) / SB;
-        const u32x4* wbase = (const u32x4*)packed + (size_t)nb * KS * 64 + lane;
-        const uint8_t* srec = packed + s_off + (size_t)nb * NG * kScaleRecBytes + (lane & 31) * 8;
-        const uint8_t* zrec = packed + z_off + (size_t)nb * NG * kZeroRecBytes + (lane & 31) * 2;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[t] = f32x16{};
 
-        // Weights of this wave's batch in super-batch j.  Loads are issued
-        // unconditionally (exact wait counts for the compiler); past the end
-        // they re-read the segment's last step (values never used).
-        auto load_w = [&](Batch& b, int j) {
-            const int sb = kb + j * SB + wave * SK_U;
-            const bool real = sb < ke;
+    auto compute = [&](const Batch& b, int nv, auto ex) {
 #pragma unroll
-            for (int q = 0; q < NGB; ++q) {
-                const int g = (real ? min(sb + q * SPG, ke - 1) : ke - 1) / GS;
-                b.sc[q] = *(const u32x2*)(srec + (size_t)g * kScaleRecBytes);
-                b.zw[q] = SYM ? 0u : (uint32_t)*(const uint16_t*)(zrec + (size_t)g * kZeroRecBytes);
-            }
+        for (int q = 0; q < NGB; ++q) {
+            if (q * SPG >= nv) break;
+            ColParams<DT> prm[4];
 #pragma unroll
-            for (int u = 0; u < SK_U; ++u) {
-                const int s = real ? min(sb + u, ke - 1) : ke - 1;
-                b.w[u] = load_weights(wbase + (size_t)s * 64);
-            }
-        };
-
-        // Activation tile of super-batch j: MB rows (rows >= M repeat row
-        // M-1), 16*SB reduction indices (past K: column K-8, never used);
-        // thread chunk i covers row c / XCPR, 8 halves at 8 * (c % XCPR).
-        u32x4 xr[XCH];
-        auto load_x = [&](int j) {
+            for (int t = 0; t < 4; ++t) prm[t] = tile_params<DT, SYM>(b.sc[q], b.zw[q], t);
 #pragma unroll
-            for (int i = 0; i < XCH; ++i) {
-                const int c = tid + SK_WAVES * 64 * i;
-                const int r = min(c / XCPR, M - 1);
-                const int k = min(kKStep * (kb + j * SB) + 8 * (c % XCPR), K - 8);
-                xr[i] = *(const u32x4*)(X + (size_t)r * K + k);
-            }
-        };
-        auto store_x = [&](int buf) {
+            for (int uu = 0; uu < SPG; ++uu) {
+                const int u = q * SPG + uu;
+                if (u >= nv) break;
 #pragma unroll
-            for (int i = 0; i < XCH; ++i) {
-                const int c = tid + SK_WAVES * 64 * i;
-                *(u32x4*)&xs[(buf * MB + c / XCPR) * XP + 8 * (c % XCPR)] = xr[i];
-            }
-        };
-
-        auto compute = [&](const Batch& b, int j, auto ex) {
-            const int nvalid = min(SK_U, ke - (kb + j * SB + wave * SK_U));   // <= 0 past the end
-            const uint16_t* xa = &xs[((j & 1) * MB + arow) * XP + wave * SK_U * kKStep + 8 * (lane >> 5)];
-#pragma unroll
-            for (int q = 0; q < NGB; ++q) {
-                if (q * SPG >= nvalid) break;
-                ColParams<DT> prm[4];
-#pragma unroll
-                for (int t = 0; t < 4; ++t) prm[t] = tile_params<DT, SYM>(b.sc[q], b.zw[q], t);
-#pragma unroll
-                for (int uu = 0; uu < SPG; ++uu) {
-                    const int u = q * SPG + uu;
-                    if (u >= nvalid) break;
-                    const u32x4 a = *(const u32x4*)(xa + kKStep * u);
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        const u32x4 bop = dequant_sel<decltype(ex)::value>(b.w[u][t], prm[t]);
-                        acc[t] = mfma32x32x16<DT>(a, bop, acc[t]);
-                    }
+                for (int t = 0; t < 4; ++t) {
+                    const u32x4 bop = dequant_sel<decltype(ex)::value>(b.w[u][t], prm[t]);
+                    acc[t] = mfma32x32x16<DT>(b.x[u], bop, acc[t]);
                 }
             }
-        };
-
-        // NBUF register buffers rotate: super-batch j computes while the next
-        // NBUF-1 of this wave's batches are in flight.  One loop exit; the
-        // super-batch count is rounded up to NBUF with empty trailing rounds.
-        auto mainloop = [&](auto ex) {
-            Batch bw[NBUF];
-#pragma unroll
-            for (int r = 0; r < NBUF - 1; ++r) load_w(bw[r], r);
-            load_x(0);
-            store_x(0);
-            __syncthreads();
-            int jj = 0;
-            do {
-#pragma unroll
-                for (int r = 0; r < NBUF; ++r) {
-                    const int j = jj + r;
-                    load_w(bw[(r + NBUF - 1) % NBUF], j + NBUF - 1);
-                    load_x(j + 1);
-                    compute(bw[r], j, ex);
-                    store_x((j + 1) & 1);
-                    __syncthreads();
-                }
-                jj += NBUF;
-            } while (jj < nsb);
-        };
-
-#pragma unroll
-        for (int t = 0; t < 4; ++t) acc[t] = f32x16{};
-        if (exact)
-            mainloop(std::true_type{});
-        else
-            mainloop(std::false_type{});
-
-        // Reduce the 8 waves' tiles through LDS (reusing the activation
-        // buffers): halve the active waves each round, always adding slot w
-        // into wave w (a fixed order).
-#pragma unroll
-        for (int h = SK_WAVES / 2; h >= 1; h >>= 1) {
-            if (wave >= h && wave < 2 * h) {
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        red[wave - h][t][q][lane] = f32x4{acc[t][4 * q], acc[t][4 * q + 1],
-                                                          acc[t][4 * q + 2], acc[t][4 * q + 3]};
-            }
-            __syncthreads();
-            if (wave < h) {
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const f32x4 v = red[wave][t][q][lane];
-                        acc[t][4 * q] += v.x;
-                        acc[t][4 * q + 1] += v.y;
-                        acc[t][4 * q + 2] += v.z;
-                        acc[t][4 * q + 3] += v.w;
-                    }
-            }
-            __syncthreads();
         }
+    };
 
-        const int64_t colw = (int64_t)nb * kColBlock + lcol;
-        if (kb == 0 && ke == KS) {
-            // the whole column block is this workgroup's: write Y directly
-            if (wave == 0) {
-                uint16_t* ybase = Y + (int64_t)lrow * N + colw;
+    auto to_slot = [&]() {
 #pragma unroll
-                for (int t = 0; t < 4; ++t)
+        for (int q = 0; q < QMAX; ++q) {
+            if (q >= QM) break;
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int r0 = 8 * (r >> 2) + (r & 3);
-                        if (r0 + lrow < M) ybase[(int64_t)r0 * N + 32 * t] = round_out<DT>(acc[t][r]);
-                    }
-            }
-            continue;
+            for (int t = 0; t < 4; ++t)
+                slots[wave][t][q][lane] = f32x4{acc[t][4 * q], acc[t][4 * q + 1],
+                                                acc[t][4 * q + 2], acc[t][4 * q + 3]};
         }
+    };
 
-        // Partial tile: rows < M only; float index (t*M + row)*32 + col.
-        const int first = (int)(((int64_t)nb * KS) / L);
-        const int last = (int)(((int64_t)(nb + 1) * KS - 1) / L);
-        const int ncontrib = last - first + 1;
-        const int slot_floats = 4 * M * 32;
-        float* slots = part + (size_t)nb * maxc * slot_floats;
-        if (wave == 0) {
-            float* pbase = slots + (size_t)(wg - first) * slot_floats + lrow * 32 + lcol;
+    // Accumulators of a whole column block straight to Y.
+    auto to_y = [&](int nb) {
+        uint16_t* ybase = Y + (size_t)(4 * (lane >> 5)) * N + (size_t)nb * kColBlock + (lane & 31);
+#pragma unroll
+        for (int q = 0; q < QMAX; ++q) {
+            if (q >= QM) break;
 #pragma unroll
             for (int t = 0; t < 4; ++t)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int r0 = 8 * (r >> 2) + (r & 3);
-                    if (r0 + lrow < M) st_dev(&pbase[(t * M + r0) * 32], acc[t][r]);
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 8 * q + 4 * (lane >> 5) + i;
+                    if (row < M) ybase[(size_t)(8 * q + i) * N + 32 * t] = round_out<DT>(acc[t][4 * q + i]);
                 }
         }
-        if (!arrive_last(&cnt[nb], ncontrib, &s_last)) continue;
+    };
 
-        // Last arrival: all threads add the slots in workgroup order.
-        for (int f = tid; f < slot_floats; f += SK_WAVES * 64) {
-            float sum = ld_dev(&slots[f]);
-            int c = 1;
-            for (; c + 3 < ncontrib; c += 4) {
-                const float v1 = ld_dev(&slots[(size_t)c * slot_floats + f]);
-                const float v2 = ld_dev(&slots[(size_t)(c + 1) * slot_floats + f]);
-                const float v3 = ld_dev(&slots[(size_t)(c + 2) * slot_floats + f]);
-                const float v4 = ld_dev(&slots[(size_t)(c + 3) * slot_floats + f]);
-                sum = (((sum + v1) + v2) + v3) + v4;
+    // Waves w and w + SK_WAVES/2 share a SIMD, whose arbiter favours the
+    // older wave: left alone, that wave runs ahead and the other finishes its
+    // equal share by itself at the end, without a partner to overlap its
+    // matrix instructions with.  The wave that is behind its partner takes
+    // the higher issue priority.
+    // (LDS accesses through the __shared__ array itself: a generic pointer
+    // would turn them into flat accesses, which count as vector memory
+    // operations and would make the loop wait for every load in flight.)
+    auto balance = [&](int done_batches) {
+        __hip_atomic_store(&s_prog[wave], done_batches, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_WORKGROUP);
+        const int partner = __builtin_amdgcn_readfirstlane(__hip_atomic_load(
+            &s_prog[wave ^ (SK_WAVES / 2)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+        if (done_batches > partner)
+            __builtin_amdgcn_s_setprio(0);
+        else
+            __builtin_amdgcn_s_setprio(1);
+    };
+
+    auto mainloop = [&](auto ex) {
+        Batch bf[SK_NBUF];
+        issue(bf[0]);
+        issue(bf[1]);
+        if (lane == 0) s_prog[wave] = 0;
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0) only: the first loads stay in flight
+        __builtin_amdgcn_s_barrier();
+        int nbC = hb, iC = ib, b = 0;
+        // One loop exit; the batch count is rounded up to SK_NBUF with empty
+        // trailing rounds (their loads are the harmless dummies above).
+        do {
+#pragma unroll
+            for (int r = 0; r < SK_NBUF; ++r) {
+                issue(bf[(r + SK_NBUF - 1) % SK_NBUF]);
+                if (b < len) {
+                    compute(bf[r], min(SK_U, KS - iC * SK_U), ex);
+                    const bool block_end = iC == nbat - 1;
+                    const bool range_end = b == len - 1;
+                    if (block_end || range_end) {
+                        if (block_end && (nbC != hb || s_w % nbat == 0)) {
+                            to_y(nbC);             // a whole block
+                        } else if (!range_end) {
+                            to_slot();             // the head
+                        }
+                        if (!range_end) {
+#pragma unroll
+                            for (int t = 0; t < 4; ++t) acc[t] = f32x16{};
+                        }
+                    }
+                    if (++iC == nbat) {
+                        iC = 0;
+                        ++nbC;
+                    }
+                    balance(b + 1);
+                }
+                ++b;
             }
-            for (; c < ncontrib; ++c) sum += ld_dev(&slots[(size_t)c * slot_floats + f]);
-            const int col = f & 31;
-            const int rr = (f >> 5) % M;
-            const int t = (f >> 5) / M;
-            Y[(int64_t)rr * N + (int64_t)nb * kColBlock + 32 * t + col] = round_out<DT>(sum);
-        }
-        if (tid == 0) reset_counter(&cnt[nb]);
-        __syncthreads();   // the LDS tiles are reused by the next segment
+        } while (b < len);
+        __hip_atomic_store(&s_prog[wave], 1 << 30, __ATOMIC_RELAXED,   // finished: never
+                           __HIP_MEMORY_SCOPE_WORKGROUP);               // hold the partner back
+        __builtin_amdgcn_s_setprio(0);
+    };
+    if (exact)
+        mainloop(std::true_type{});
+    else
+        mainloop(std::false_type{});
+
+    // ---- workgroup epilogue: the partial blocks in increasing order.
+    auto B0_of = [&](int g) { return range_start(g * SK_WAVES, base, rem); };   // first batch of g
+    if (lane == 0) s_parts[wave] = wave_parts(s_w, s_w + len, nbat);
+    __syncthreads();
+    const int my_tail = s_parts[wave].tail;
+    // Elements of a partial tile: (t, q) pairs of f32x4 per lane, pair t*QM + q
+    // handled by wave (t*QM + q) % SK_WAVES.
+    auto mine = [&](int t, int q) { return q < QM && ((t * QM + q) % SK_WAVES) == wave; };
+    int done = -1;
+    for (int p = 0; p < 2 * SK_WAVES; ++p) {
+        const WaveParts pw = s_parts[p >> 1];
+        const int nb = (p & 1) ? pw.tail : pw.head;
+        if (nb < 0 || nb == done) continue;
+        done = nb;
+        __syncthreads();   // the previous block's slots have been read
+        if (my_tail == nb) to_slot();
+        __syncthreads();
+        const bool inside = nb * nbat >= B0_of(wg) && (nb + 1) * nbat <= B0_of(wg + 1);
+        const int row0 = 4 * (lane >> 5);
+        const size_t col0 = (size_t)nb * kColBlock + (lane & 31);
+        // Shared with other workgroups: partial tile [t][row < M][32] into
+        // this workgroup's workspace slot 0 (its first block) or 1 (its last).
+        const int g0 = inside ? 0 : wave_of_batch(nb * nbat, base, rem) / SK_WAVES;
+        const int g1 = inside ? 0 : wave_of_batch((nb + 1) * nbat - 1, base, rem) / SK_WAVES;
+        const int tile_floats = 4 * M * 32;
+        // Workgroups after g0 start inside block nb (their slot 0); g0 holds
+        // it as its last block (slot 1) unless its range starts at nb too.
+        const int s0 = inside ? 0 : 2 * g0 + (nb == B0_of(g0) / nbat ? 0 : 1);
+        auto slot_of = [&](int g) {
+            return part + (size_t)(g == g0 ? s0 : 2 * g) * tile_floats;
+        };
+        float* my_slot = slot_of(wg);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int q = 0; q < QMAX; ++q) {
+                if (!mine(t, q)) continue;
+                // the workgroup's partial of block nb: slots added in wave order
+                f32x4 v = f32x4{};
+                bool first = true;
+#pragma unroll
+                for (int w = 0; w < SK_WAVES; ++w) {
+                    const WaveParts ow = s_parts[w];
+                    if (ow.head != nb && ow.tail != nb) continue;
+                    const f32x4 sv = slots[w][t][q][lane];
+                    v = first ? sv : v + sv;
+                    first = false;
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int row = 8 * q + row0 + j;
+                    if (row >= M) continue;
+                    if (inside)
+                        Y[(size_t)row * N + col0 + 32 * t] = round_out<DT>(v[j]);
+                    else
+                        st_dev(&my_slot[(t * M + row) * 32 + (lane & 31)], v[j]);
+                }
+            }
+        if (inside) continue;
+        if (!arrive_last(&cnt[g0], g1 - g0 + 1, &s_last)) continue;
+        // Last arrival: add the workgroups' tiles in workgroup order; thread
+        // tid handles column tid % 32 of rows tid / 32 and tid / 32 + 16.
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int row = (tid >> 5) + 16 * i;
+                if (row >= M) continue;
+                const int f = (t * M + row) * 32 + (tid & 31);
+                float sum = ld_dev(&slot_of(g0)[f]);
+                for (int g = g0 + 1; g <= g1; ++g) sum += ld_dev(&slot_of(g)[f]);
+                Y[(size_t)row * N + (size_t)nb * kColBlock + 32 * t + (tid & 31)] = round_out<DT>(sum);
+            }
+        if (tid == 0) reset_counter(&cnt[g0]);
     }
 }
 
@@ -604,7 +644,7 @@ void launch_splitk_mb(const void* X, const void* packed, void* Y, int64_t M, con
                       const Plan& p, float* part, uint32_t* cnt, hipStream_t stream) {
     hipLaunchKernelGGL((splitk_kernel<DT, SYM, GS, MB>), dim3(p.grid_x), dim3(SK_WAVES * 64), 0,
                        stream, (const uint16_t*)X, (const uint8_t*)packed, (uint16_t*)Y, part, cnt,
-                       (int)M, (int)L.N, (int)L.K, p.steps_per_split, p.splits, L.s_off, L.z_off,
+                       (int)M, (int)L.N, (int)L.K, p.nbat, p.base, p.rem, L.s_off, L.z_off,
                        L.t_off);
 }
 

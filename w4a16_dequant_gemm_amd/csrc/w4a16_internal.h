@@ -11,12 +11,18 @@ namespace w4a16 {
 
 enum Variant { VARIANT_SPLITK = 0, VARIANT_TILED = 1 };
 
+// Split-K kernel geometry, shared by the plan and the kernel.
+constexpr int kSplitKWaves = 8;   // waves per workgroup (two per SIMD), one workgroup per CU
+constexpr int kSplitKBatch = 4;   // k-steps per batch
+
 // How one w4a16_gemm call is executed.  Computed on the host from the shape
 // only, so w4a16_workspace_bytes and w4a16_gemm always agree.
 struct Plan {
     Variant variant;
     int splits;            // S: workgroups that share one output tile along K
-    int steps_per_split;   // k-steps per split (tiled) / per wave (split-K)
+    int steps_per_split;   // k-steps per split (tiled)
+    int nbat;              // split-K: batches (kSplitKBatch k-steps) per column block
+    int base, rem;         // split-K: wave w owns base (+1 if w < rem) batches
     int mt;                // 32-row MFMA tiles per wave
     int waves;             // waves per workgroup
     int grid_x, grid_y, grid_z;
