@@ -32,6 +32,28 @@ DEFAULT_WORKLOAD = "decode_m1_k8192_n28672_fp16_asym_g128_outliers"
 METRIC = "W4A16 GEMM achieved HBM GB/s"
 
 
+_SLEEP_CYCLES_PER_MS = None
+
+
+def hold_gpu(ms):
+    """Enqueue a GPU spin of about `ms` milliseconds on the current stream.
+    Launches queued behind it then run back to back, so per-launch events
+    time the kernels and not the host's launch overhead."""
+    import torch
+
+    global _SLEEP_CYCLES_PER_MS
+    if _SLEEP_CYCLES_PER_MS is None:
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        torch.cuda._sleep(2_000_000)
+        b.record()
+        torch.cuda.synchronize()
+        _SLEEP_CYCLES_PER_MS = 2_000_000 / max(a.elapsed_time(b), 1e-3)
+    torch.cuda._sleep(int(ms * _SLEEP_CYCLES_PER_MS))
+
+
 def algorithmic_bytes(cfg):
     M, K, N, G = cfg["M"], cfg["K"], cfg["N"], cfg["G"]
     b = K * N // 2 + (K // G) * N * 2 + M * K * 2 + M * N * 2
@@ -138,38 +160,63 @@ def run_workload(name, steps, warmup, rotate_bytes=1 << 30, with_cpu=True, compa
     stream = torch.cuda.current_stream()
 
     def step(i):
-        w4.w4a16_gemm(X, blobs[i % copies], Y=Y, workspace=ws, stream=stream)
+        # the current stream: the default one, or the capture stream below
+        w4.w4a16_gemm(X, blobs[i % copies], Y=Y, workspace=ws)
 
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
+    # host time to queue one step (Python + launch), to size the GPU holds below
+    h0 = time.perf_counter()
+    for i in range(10):
+        step(i)
+    host_ms = (time.perf_counter() - h0) * 1e3 / 10
+    torch.cuda.synchronize()
+    # Timed region: exactly `steps` calls, captured once into a HIP graph and
+    # replayed between two events, so the GPU runs them back to back without
+    # the host's per-call launch cost (the graph is built outside the region).
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(steps):
+            step(i)
+    torch.cuda.synchronize()
+    graph.replay()               # one untimed replay
+    torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t0.record(stream)
-    for i in range(steps):
-        ev[i][0].record(stream)
-        step(i)
-        ev[i][1].record(stream)
+    graph.replay()
     t1.record(stream)
     torch.cuda.synchronize()
     ms_total = t0.elapsed_time(t1)
     ms_step = ms_total / steps
+    del graph
+    # Per-launch durations for the roofline: a second pass with an event pair
+    # around every call (the pairs themselves add a little GPU time).
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    hold_gpu(5.0 + 3.0 * host_ms * steps)
+    for i in range(steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
     per_launch = np.array([a.elapsed_time(b) for a, b in ev])
     kern_ms = float(np.mean(per_launch))
 
     nbytes = algorithmic_bytes(cfg)
     flops = algorithmic_flops(cfg)
     bound = bound_of(cfg)
+    # the timed region holds nothing but back-to-back launches of the kernel,
+    # so its average per step is the kernel's average launch duration
     if bound == "hbm":
-        achieved = nbytes / (kern_ms * 1e-3) / 1e9
+        achieved = nbytes / (ms_step * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(name)}
     else:
-        achieved = flops / (kern_ms * 1e-3) / 1e12
+        achieved = flops / (ms_step * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_TFLOPS, 4),
                 "traffic": measured_traffic(name)}
@@ -189,14 +236,15 @@ def run_workload(name, steps, warmup, rotate_bytes=1 << 30, with_cpu=True, compa
         "config": {"workload": name, "M": p.M, "K": p.K, "N": p.N, "group_size": p.G,
                    "act_dtype": p.dtype, "quant": "sym" if p.sym else "asym",
                    "outlier_cols": cfg.get("outlier_frac", 0.0), "parallelism": "none (1 GPU)",
-                   "cold_weight_copies": copies},
-        "kernel_us": round(kern_ms * 1e3, 3),
-        "kernel_us_p10_p50_p90": [round(float(np.percentile(per_launch, q)) * 1e3, 3)
-                                  for q in (10, 50, 90)],
-        "tflops": round(flops / (kern_ms * 1e-3) / 1e12, 2),
+                   "cold_weight_copies": copies, "launch": "hip_graph_replay"},
+        "kernel_us": round(ms_step * 1e3, 3),
+        "host_us_per_call": round(host_ms * 1e3, 2),
+        "kernel_us_event_pairs_mean_p10_p50_p90": [round(kern_ms * 1e3, 3)] + [
+            round(float(np.percentile(per_launch, q)) * 1e3, 3) for q in (10, 50, 90)],
+        "tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
         "algorithmic_bytes": nbytes,
         "kernel_source_hash": kernel_source_hash(),
-        "weight_only_gbs": round((p.K * p.N // 2) / (kern_ms * 1e-3) / 1e9, 1),
+        "weight_only_gbs": round((p.K * p.N // 2) / (ms_step * 1e-3) / 1e9, 1),
         "roofline": roof,
     }
     if comparators:
@@ -224,6 +272,7 @@ def comparator_times(p, X, blobs, copies, stream, reps=20):
             torch.cuda.synchronize()
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
+            hold_gpu(5.0 + 0.15 * reps)
             a.record(stream)
             for i in range(reps):
                 fn(i)
@@ -257,7 +306,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; the W4A16 path "
-                                   "has no multi-GPU mode (see the sharding notes in DESIGN.md)",
+                                   "has no multi-GPU mode (a caller shards N across GPUs)",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
     if args.calibration_copy_mib > 0:

@@ -45,6 +45,8 @@ class W4A16Error(RuntimeError):
 
 
 _lib = None
+_layout_version = None
+_ws_bytes = {}
 
 
 def load_library(path: str = LIB_PATH):
@@ -76,6 +78,9 @@ def load_library(path: str = LIB_PATH):
     lib.w4a16_dequant.restype = ci
     lib.w4a16_mfma_layout_probe.argtypes = [p, p, p, u32, p]
     lib.w4a16_mfma_layout_probe.restype = ci
+    global _layout_version
+    _layout_version = lib.w4a16_layout_version()
+    _ws_bytes.clear()
     _lib = lib
     return lib
 
@@ -125,6 +130,16 @@ def w4a16_packed_bytes(K: int, N: int, group_size: int, flags: int) -> int:
 
 def w4a16_workspace_bytes(M: int, N: int, K: int, group_size: int, flags: int) -> int:
     return int(load_library().w4a16_workspace_bytes(M, N, K, group_size, flags))
+
+
+def _workspace_need(M, N, K, G, flags) -> int:
+    # the plan depends on the shape and on the W4A16_* environment overrides
+    key = (M, N, K, G, flags, os.environ.get("W4A16_FORCE_VARIANT"),
+           os.environ.get("W4A16_SPLITK_WGS"), os.environ.get("W4A16_SPLITS"))
+    need = _ws_bytes.get(key)
+    if need is None:
+        need = _ws_bytes[key] = w4a16_workspace_bytes(M, N, K, G, flags)
+    return need
 
 
 @dataclass
@@ -183,7 +198,8 @@ def w4a16_gemm(X: torch.Tensor, packed: PackedW4, M: Optional[int] = None,
                Y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                stream=None) -> torch.Tensor:
     """Y[M][N] = X[M][K] . dequant(packed); X is [M][K] fp16/bf16 on the device."""
-    if packed.layout_version != w4a16_layout_version():
+    lib = load_library()
+    if packed.layout_version != _layout_version:
         raise W4A16Error(W4A16_ERR_INVALID_ARG, "w4a16_gemm (blob layout version)")
     K, N, G, flags = packed.K, packed.N, packed.group_size, packed.flags
     if M is None:
@@ -192,13 +208,11 @@ def w4a16_gemm(X: torch.Tensor, packed: PackedW4, M: Optional[int] = None,
         raise W4A16Error(W4A16_ERR_INVALID_ARG, "w4a16_gemm (X dtype/shape)")
     if Y is None:
         Y = torch.empty((M, N), dtype=X.dtype, device=X.device)
-    need = w4a16_workspace_bytes(M, N, K, G, flags)
     if workspace is None:
-        workspace = workspace_for(need, X.device)
-    _check(load_library().w4a16_gemm(_ptr(X), _ptr(packed.data), packed.data.numel(), _ptr(Y),
-                                     M, N, K, G, flags, _ptr(workspace),
-                                     0 if workspace is None else workspace.numel(),
-                                     _stream(stream)), "w4a16_gemm")
+        workspace = workspace_for(_workspace_need(M, N, K, G, flags), X.device)
+    _check(lib.w4a16_gemm(_ptr(X), _ptr(packed.data), packed.data.numel(), _ptr(Y), M, N, K, G,
+                          flags, _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                          _stream(stream)), "w4a16_gemm")
     return Y
 
 

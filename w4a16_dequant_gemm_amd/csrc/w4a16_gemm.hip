@@ -298,8 +298,8 @@ __global__ __launch_bounds__(SK_WAVES * 64) void splitk_kernel(
 
     auto mainloop = [&](auto ex) {
         Batch bf[SK_NBUF];
-        issue(bf[0]);
-        issue(bf[1]);
+#pragma unroll
+        for (int i = 0; i < SK_NBUF - 1; ++i) issue(bf[i]);
         if (lane == 0) s_prog[wave] = 0;
         __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0) only: the first loads stay in flight
         __builtin_amdgcn_s_barrier();
