@@ -111,13 +111,15 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int G, uint32_t /*flags*/) {
     } else {
         p.variant = VARIANT_TILED;
         p.mt = M <= 64 ? 2 : 4;
-        p.waves = 4;
+        p.waves = 8;
         const int64_t CG = ceil_div(NB, 4);
         const int64_t RB = ceil_div(M, 32 * p.mt);
         const int64_t tiles = CG * RB;
-        const int64_t slots = (int64_t)kNumCUs * (p.mt == 2 ? 2 : 1);
+        // Split K over workgroups when there are fewer tiles than CUs, as far
+        // as one round of workgroups (one per CU) goes: measured on MI355X, a
+        // second round or more partial tiles cost more than they gain.
         int64_t s = 1;
-        if (tiles < slots) s = ceil_div(slots, tiles);
+        if (tiles < kNumCUs) s = kNumCUs / tiles;
         if (s > kMaxSplits) s = kMaxSplits;
         if (forced_splits > 0) s = forced_splits < kMaxSplits ? forced_splits : kMaxSplits;
         // at least 4 stages per split

@@ -45,6 +45,32 @@ namespace w4a16 {
 namespace {
 
 
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
+// at lds + 16*l (lds must be wave-uniform).  The builtin exists only for the
+// device target, so the host pass sees an empty body.
+__device__ __forceinline__ void load_to_lds16(const void* g, void* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+#else
+    (void)g;
+    (void)lds;
+#endif
+}
+
+// Workgroup barrier after this wave's loads (copies into LDS included) and
+// LDS operations have all completed.
+__device__ __forceinline__ void stage_barrier_all() {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Workgroup barrier between LDS stages: waits for this wave's LDS operations
+// only, not for its vector memory loads (which stay in flight across it; the
+// compiler waits for each where its value is used).  The asm statement also
+// keeps the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void stage_barrier_lds() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ u32x4 load_weights(const u32x4* p) {
     return __builtin_nontemporal_load(p);   // streamed once: do not keep in cache
 }
@@ -422,134 +448,232 @@ __global__ __launch_bounds__(SK_WAVES * 64) void splitk_kernel(
 
 // ---------------------------------------------------------------------------
 // LDS-tiled kernel, M > 32.
+//
+// A workgroup of 8 waves owns ROWS = 32*MT rows by 512 columns.  Wave w
+// owns the 64 columns of half w/4 of column block 4*blockIdx.x + w%4 for
+// all ROWS rows: it dequantizes each of its weight words once and feeds it
+// to MT row tiles.  Two waves share a SIMD (w and w+4), so one wave's
+// dequantization runs while the other's matrix instructions execute -- a
+// wave does not issue vector ALU work while its own MFMA executes, so a
+// single wave per SIMD would add the two.  The activation tile of a stage
+// (KT k-steps) is staged through LDS (copied straight into it for MT = 4),
+// two or three stages deep, one barrier per stage.  LDS layout: 16-byte slot (row, chunk) holds halves 8*chunk..+7 of
+// the stage's k range for that row, at position row*16 + (chunk ^ (row & 15))
+// -- the XOR spreads the 16 rows a quarter-wave reads at one chunk over all
+// banks.  Inside a stage the next k-step's A operands (LDS) and B operands
+// (dequantized weights) are prepared before the current k-step's MFMAs.
 // ---------------------------------------------------------------------------
+constexpr int TK_WAVES = 8;
+
 template <int DT, bool SYM, int GS, int MT>
-__global__ __launch_bounds__(256) void tiled_kernel(
+__global__ __launch_bounds__(TK_WAVES * 64) void tiled_kernel(
     const uint16_t* __restrict__ X, const uint8_t* __restrict__ packed, uint16_t* __restrict__ Y,
     float* __restrict__ part, uint32_t* __restrict__ cnt, int M, int N, int K,
     int steps_per_split, int S, size_t s_off, size_t z_off, size_t t_off) {
-    constexpr int KT = MT == 4 ? 4 : 8;         // k-steps per stage (fits the registers)
+    constexpr int KT = 8;                       // k-steps per stage
     constexpr int ROWS = 32 * MT;
-    constexpr int LDX = KT * kKStep + 8;        // LDS row pitch in halves (+16 B against bank conflicts)
+    constexpr int CPR = 2 * KT;                 // 16-byte chunks per row and stage
+    constexpr int SLOTS = ROWS * CPR;           // 16-byte slots per stage buffer
+    constexpr int XI = SLOTS / (TK_WAVES * 64); // direct loads per thread and stage
     constexpr int SPG = GS < KT ? GS : KT;      // k-steps per group inside a stage
     constexpr int NGST = KT / SPG;              // groups per stage
-    constexpr int XCH = ROWS * KT * kKStep / 8 / 256;   // 16-byte X chunks per thread per stage
-    __shared__ __align__(16) uint16_t xs[2][ROWS * LDX];
+    static_assert(CPR == 16, "the swizzle assumes 16 chunks per row");
+    constexpr int NW = MT == 2 ? 3 : 2;         // stages in flight (LDS buffers, weight sets)
+    __shared__ __align__(16) u32x4 xs0[SLOTS];
+    __shared__ __align__(16) u32x4 xs1[SLOTS];
+    __shared__ __align__(16) u32x4 xs2[NW == 3 ? SLOTS : 1];
     __shared__ uint32_t s_last;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    const int half = wave >> 2;                 // column tiles 2*half, 2*half+1 of the block
     const int NB = N / kColBlock;
     const int KS = K / kKStep;
     const int NG = K / (kKStep * GS);
-    const int nb = blockIdx.x * 4 + wave;
+    const int nb = blockIdx.x * 4 + (wave & 3);
     const bool nb_ok = nb < NB;
     const int nbc = nb_ok ? nb : NB - 1;
     const int m0 = blockIdx.y * ROWS;
     const int split = blockIdx.z;
-    const int s_beg = split * steps_per_split;   // a multiple of 8 (so of KT)
+    const int s_beg = split * steps_per_split;   // a multiple of KT
     const int s_end = min(KS, s_beg + steps_per_split);
     const int nst = s_end > s_beg ? (s_end - s_beg + KT - 1) / KT : 0;
 
-    const u32x4* wbase = (const u32x4*)packed + (size_t)nbc * KS * 64 + lane;
-    const uint8_t* srec = packed + s_off + (size_t)nbc * NG * kScaleRecBytes + (lane & 31) * 8;
+    // this wave's two weight words of each chunk: bytes 8*half..+7 of the lane's 16
+    const u32x2* wbase = (const u32x2*)(packed + (size_t)nbc * KS * 1024 + lane * 16 + half * 8);
+    const uint8_t* srec = packed + s_off + (size_t)nbc * NG * kScaleRecBytes + (lane & 31) * 8 + half * 4;
     const uint8_t* zrec = packed + z_off + (size_t)nbc * NG * kZeroRecBytes + (lane & 31) * 2;
 
-    struct Stage {
-        u32x2 sc[NGST];
-        uint32_t zw[NGST];
-        u32x4 w[KT];
+    // Activation copies: copy i of this thread covers slot
+    // s = (8*i + wave)*64 + lane, i.e. row s/16 (rows >= M re-read row M-1,
+    // never stored), position s%16 = lane%16, which holds chunk
+    // (lane%16) ^ (row & 15); row & 15 does not depend on i.
+    //  * MT = 4: straight from global memory into LDS (global_load_lds, no
+    //    registers: MT = 4 has none to spare).  The compiler cannot tell
+    //    which loads such a copy depends on and waits for all loads in
+    //    flight before it next reads a loaded register, so the next stage's
+    //    loads are issued only after this stage's first operands are read.
+    //  * MT = 2: global -> VGPR one stage ahead of the LDS store, which keeps
+    //    every wait exact and allows a third stage in flight.
+    constexpr bool DMA = MT == 4;
+    const int xchunk = (lane & 15) ^ ((4 * wave + (lane >> 4)) & 15);
+    const uint16_t* xrow[XI];
+#pragma unroll
+    for (int i = 0; i < XI; ++i)
+        xrow[i] = X + (size_t)min(m0 + (TK_WAVES * i + wave) * 4 + (lane >> 4), M - 1) * K;
+    u32x4 xr[DMA ? 1 : XI];
+    auto x_col = [&](int si) {
+        const int st = s_beg + min(si, nst - 1) * KT;
+        return min(kKStep * st + 8 * xchunk, K - 8);   // past K: never used
+    };
+    auto load_x = [&](int si) {   // MT = 2: into xr
+        const int kk = x_col(si);
+#pragma unroll
+        for (int i = 0; i < (DMA ? 0 : XI); ++i) xr[i] = *(const u32x4*)(xrow[i] + kk);
+    };
+    auto store_x = [&](u32x4* buf) {
+#pragma unroll
+        for (int i = 0; i < (DMA ? 0 : XI); ++i) buf[(TK_WAVES * i + wave) * 64 + lane] = xr[i];
+    };
+    auto copy_x = [&](u32x4* buf, int si) {   // MT = 4: straight into LDS
+        const int kk = x_col(si);
+#pragma unroll
+        for (int i = 0; i < XI; ++i) load_to_lds16(xrow[i] + kk, &buf[(TK_WAVES * i + wave) * 64]);
     };
 
-    // X stage copy: chunk c = tid + 256*i covers row c / (2*KT) of the tile,
-    // 8 halves at column 8 * (c % (2*KT)).  Rows >= M re-read row M-1 and
-    // columns >= K re-read column K-8 (never used), so loads are unconditional.
-    auto load_x = [&](u32x4 (&xr)[XCH], int si) {
-        const int st = s_beg + min(si, nst - 1) * KT;
-#pragma unroll
-        for (int i = 0; i < XCH; ++i) {
-            const int c = tid + 256 * i;
-            const int row = min(m0 + c / (KT * 2), M - 1);
-            const int kk = min(kKStep * st + 8 * (c % (KT * 2)), K - 8);
-            xr[i] = *(const u32x4*)(X + (size_t)row * K + kk);
-        }
-    };
-    auto store_x = [&](int buf, const u32x4 (&xr)[XCH]) {
-#pragma unroll
-        for (int i = 0; i < XCH; ++i) {
-            const int c = tid + 256 * i;
-            *(u32x4*)&xs[buf][(c / (KT * 2)) * LDX + 8 * (c % (KT * 2))] = xr[i];
-        }
+    struct Stage {
+        uint32_t sc[NGST];
+        uint32_t zw[NGST];
+        u32x2 w[KT];
     };
     auto load_w = [&](Stage& b, int si) {
         const int st = s_beg + min(si, nst - 1) * KT;
 #pragma unroll
         for (int j = 0; j < NGST; ++j) {
             const int g = min(st + j * SPG, s_end - 1) / GS;
-            b.sc[j] = *(const u32x2*)(srec + (size_t)g * kScaleRecBytes);
+            b.sc[j] = *(const uint32_t*)(srec + (size_t)g * kScaleRecBytes);
             b.zw[j] = SYM ? 0u : (uint32_t)*(const uint16_t*)(zrec + (size_t)g * kZeroRecBytes);
         }
 #pragma unroll
-        for (int u = 0; u < KT; ++u) b.w[u] = load_weights(wbase + (size_t)min(st + u, s_end - 1) * 64);
+        for (int u = 0; u < KT; ++u)
+            b.w[u] = __builtin_nontemporal_load(wbase + (size_t)min(st + u, s_end - 1) * 128);
     };
 
-    f32x16 acc[MT][4];
+    f32x16 acc[MT][2];
 #pragma unroll
     for (int r = 0; r < MT; ++r)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) acc[r][t] = f32x16{};
+        for (int tt = 0; tt < 2; ++tt) acc[r][tt] = f32x16{};
 
-    auto compute = [&](const Stage& b, int buf, int si, auto exact) {
+    // A operand of row tile r at k-step u: row 32r + lane%32, chunk
+    // 2u + lane/32, stored at position (2u + lane/32) ^ (lane & 15) =
+    // 2u ^ ((lane/32) ^ (lane & 15)).
+    const int aswz = (lane >> 5) ^ (lane & 15);
+    const int arow = (lane & 31) * CPR;
+    // issue_ahead() issues the loads of a later stage once this stage's
+    // first operands are in registers (so no wait for them can also wait for
+    // the younger loads).
+    auto compute = [&](const Stage& b, const u32x4* buf, int si, auto exact, auto issue_ahead) {
         const int nvalid = min(KT, s_end - (s_beg + si * KT));   // <= 0 past the end
-        const uint16_t* xb = &xs[buf][(lane & 31) * LDX + 8 * (lane >> 5)];
+        auto read_a = [&](u32x4 (&a)[MT], int u) {
 #pragma unroll
-        for (int j = 0; j < NGST; ++j) {
-            if (j * SPG >= nvalid) break;
-            ColParams<DT> prm[4];
+            for (int r = 0; r < MT; ++r) a[r] = buf[arow + 32 * CPR * r + ((2 * u) ^ aswz)];
+        };
+        auto make_b = [&](u32x4 (&bo)[2], int u) {
+            const int j = u / SPG;
+            const u32x2 sc2 = {b.sc[j], b.sc[j]};
 #pragma unroll
-            for (int t = 0; t < 4; ++t) prm[t] = tile_params<DT, SYM>(b.sc[j], b.zw[j], t);
+            for (int tt = 0; tt < 2; ++tt) {
+                const ColParams<DT> prm = tile_params<DT, SYM>(sc2, b.zw[j], 2 * half + tt);
+                bo[tt] = dequant_sel<decltype(exact)::value>(b.w[u][tt], prm);
+            }
+        };
+        // MT = 2 prepares the next k-step's operands (A from LDS, B
+        // dequantized) before this k-step's MFMAs; MT = 4 has no registers for
+        // them and prepares each k-step's operands just before its MFMAs (the
+        // other wave on the SIMD runs meanwhile).
+        constexpr bool AHEAD = MT == 2;
+        u32x4 a[MT], bo[2];
+        read_a(a, 0);
+        make_b(bo, 0);
+        if constexpr (DMA) __builtin_amdgcn_sched_barrier(0);   // keep the loads below
+        issue_ahead();
 #pragma unroll
-            for (int uu = 0; uu < SPG; ++uu) {
-                const int u = j * SPG + uu;
-                if (u >= nvalid) break;
-                u32x4 a[MT];
-#pragma unroll
-                for (int r = 0; r < MT; ++r) a[r] = *(const u32x4*)(xb + 32 * r * LDX + kKStep * u);
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const u32x4 bop = dequant_sel<decltype(exact)::value>(b.w[u][t], prm[t]);
-#pragma unroll
-                    for (int r = 0; r < MT; ++r) acc[r][t] = mfma32x32x16<DT>(a[r], bop, acc[r][t]);
+        for (int u = 0; u < KT; ++u) {
+            if (u >= nvalid) break;
+            if constexpr (AHEAD) {
+                u32x4 an[MT], bn[2];
+                if (u + 1 < KT) {
+                    read_a(an, u + 1);
+                    make_b(bn, u + 1);
                 }
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                    for (int r = 0; r < MT; ++r) acc[r][tt] = mfma32x32x16<DT>(a[r], bo[tt], acc[r][tt]);
+                if (u + 1 < KT) {
+#pragma unroll
+                    for (int r = 0; r < MT; ++r) a[r] = an[r];
+#pragma unroll
+                    for (int tt = 0; tt < 2; ++tt) bo[tt] = bn[tt];
+                }
+            } else {
+                if (u > 0) {
+                    read_a(a, u);
+                    make_b(bo, u);
+                }
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                    for (int r = 0; r < MT; ++r) acc[r][tt] = mfma32x32x16<DT>(a[r], bo[tt], acc[r][tt]);
             }
         }
     };
 
-    // Stage i sits in LDS buffer i%2 and register set A or B; the next
-    // stage's loads are in flight while it computes.  One loop exit; a stage
-    // index >= nst loads dummies and computes nothing.
+    // NW stages in flight.  Stage i computes from LDS buffer i%NW and weight
+    // set i%NW.  MT = 2 (NW = 3), during stage i: the activations of stage i+1
+    // (in VGPRs since stage i-1) go to LDS buffer (i+1)%3, those of stage i+2
+    // are loaded into the VGPRs, and the weights of stage i+2 into set
+    // (i+2)%3 -- the activation loads first, so that waiting for them never
+    // waits for the younger weight loads; one barrier per stage, for LDS only.
+    // MT = 4 (NW = 2), during stage i: stage i+1's activations are copied into
+    // LDS buffer (i+1)%2 and its weights loaded into set (i+1)%2; the barrier
+    // at the end of stage i waits for all of them.  One loop exit; a stage
+    // index >= nst loads in-bounds dummies and computes nothing.
     auto mainloop = [&](auto exact) {
-        Stage A, B;
-        u32x4 xr[XCH];
-        load_x(xr, 0);
-        load_w(A, 0);
-        store_x(0, xr);
-        __syncthreads();
-        int i = 0;
-        do {
-            load_x(xr, i + 1);
-            load_w(B, i + 1);
-            compute(A, 0, i, exact);
-            store_x(1, xr);
-            __syncthreads();
-            load_x(xr, i + 2);
-            load_w(A, i + 2);
-            compute(B, 1, i + 1, exact);
-            store_x(0, xr);
-            __syncthreads();
-            i += 2;
-        } while (i < nst);
+        if constexpr (NW == 3) {
+            Stage A, B, C;
+            load_x(0);
+            load_w(A, 0);
+            load_w(B, 1);
+            store_x(xs0);
+            load_x(1);
+            stage_barrier_lds();
+            int i = 0;
+            do {
+                compute(A, xs0, i, exact, [&] { store_x(xs1); load_x(i + 2); load_w(C, i + 2); });
+                stage_barrier_lds();
+                compute(B, xs1, i + 1, exact, [&] { store_x(xs2); load_x(i + 3); load_w(A, i + 3); });
+                stage_barrier_lds();
+                compute(C, xs2, i + 2, exact, [&] { store_x(xs0); load_x(i + 4); load_w(B, i + 4); });
+                stage_barrier_lds();
+                i += 3;
+            } while (i < nst);
+        } else {
+            Stage A, B;
+            copy_x(xs0, 0);
+            load_w(A, 0);
+            stage_barrier_all();
+            int i = 0;
+            do {
+                compute(A, xs0, i, exact, [&] { copy_x(xs1, i + 1); load_w(B, i + 1); });
+                stage_barrier_all();
+                compute(B, xs1, i + 1, exact, [&] { copy_x(xs0, i + 2); load_w(A, i + 2); });
+                stage_barrier_all();
+                i += 2;
+            } while (i < nst);
+        }
     };
     if (nst > 0) {
         if (uses_exact_form<DT>(packed, t_off))
@@ -558,36 +682,36 @@ __global__ __launch_bounds__(256) void tiled_kernel(
             mainloop(std::false_type{});
     }
 
-    const int64_t colw = (int64_t)nb * kColBlock + (lane & 31);
+    const int64_t colw = (int64_t)nb * kColBlock + 64 * half + (lane & 31);
     if (S == 1) {
         if (nb_ok) {
 #pragma unroll
             for (int r = 0; r < MT; ++r)
 #pragma unroll
-                for (int t = 0; t < 4; ++t)
+                for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
                         const int rr = m0 + 32 * r + acc_row(i, lane);
-                        if (rr < M) Y[(int64_t)rr * N + colw + 32 * t] = round_out<DT>(acc[r][t][i]);
+                        if (rr < M) Y[(int64_t)rr * N + colw + 32 * tt] = round_out<DT>(acc[r][tt][i]);
                     }
         }
         return;
     }
 
     // Cross-workgroup reduction; slot float index
-    // (((wave*MT + r)*4 + t)*16 + i)*64 + lane.
+    // (((wave*MT + r)*2 + tt)*16 + i)*64 + lane.
     const int tile = blockIdx.y * gridDim.x + blockIdx.x;
-    constexpr int RPW = MT * 4 * 16;   // accumulator registers per lane
-    const size_t slot_floats = (size_t)4 * RPW * 64;
+    constexpr int RPW = MT * 2 * 16;   // accumulator registers per lane
+    const size_t slot_floats = (size_t)TK_WAVES * RPW * 64;
     float* base = part + (size_t)tile * S * slot_floats + (size_t)wave * RPW * 64 + lane;
     {
         float* mine = base + (size_t)split * slot_floats;
 #pragma unroll
         for (int r = 0; r < MT; ++r)
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
+            for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) st_dev(&mine[((r * 4 + t) * 16 + i) * 64], acc[r][t][i]);
+                for (int i = 0; i < 16; ++i) st_dev(&mine[((r * 2 + tt) * 16 + i) * 64], acc[r][tt][i]);
     }
     if (!arrive_last(&cnt[tile], S, &s_last)) return;
 
@@ -595,9 +719,9 @@ __global__ __launch_bounds__(256) void tiled_kernel(
     // workgroup's own slot is read back too, so every tile is summed the same
     // way whichever workgroup is last).
 #pragma unroll 1
-    for (int rt = 0; rt < MT * 4; ++rt) {
-        const int r = rt >> 2;
-        const int t = rt & 3;
+    for (int rt = 0; rt < MT * 2; ++rt) {
+        const int r = rt >> 1;
+        const int tt = rt & 1;
         float v[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) v[i] = ld_dev(&base[(rt * 16 + i) * 64]);
@@ -610,7 +734,7 @@ __global__ __launch_bounds__(256) void tiled_kernel(
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int rr = m0 + 32 * r + acc_row(i, lane);
-                if (rr < M) Y[(int64_t)rr * N + colw + 32 * t] = round_out<DT>(v[i]);
+                if (rr < M) Y[(int64_t)rr * N + colw + 32 * tt] = round_out<DT>(v[i]);
             }
         }
     }
@@ -659,7 +783,7 @@ void launch_splitk(const void* X, const void* packed, void* Y, int64_t M, const 
 template <int DT, bool SYM, int GS>
 void launch_tiled(const void* X, const void* packed, void* Y, int64_t M, const Layout& L,
                   const Plan& p, float* part, uint32_t* cnt, hipStream_t stream) {
-    const dim3 grid(p.grid_x, p.grid_y, p.grid_z), block(256);
+    const dim3 grid(p.grid_x, p.grid_y, p.grid_z), block(TK_WAVES * 64);
     if (p.mt == 2)
         hipLaunchKernelGGL((tiled_kernel<DT, SYM, GS, 2>), grid, block, 0, stream,
                            (const uint16_t*)X, (const uint8_t*)packed, (uint16_t*)Y, part, cnt,
