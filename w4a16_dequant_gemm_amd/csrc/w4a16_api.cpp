@@ -15,7 +15,6 @@ namespace {
 
 constexpr int kNumCUs = 256;        // MI355X compute units
 constexpr int kMaxSplits = 16;
-constexpr int kTiledStage = 8;      // k-steps per tiled stage
 // Counter area at the start of every workspace: one uint32 per output tile,
 // at a fixed size for every shape, so the partial sums of one call can never
 // land where another call's counters live when callers share a workspace.

@@ -17,11 +17,15 @@
 //         fused multiply-add against a pre-multiplied zero would round the
 //         addend first and is not exact.)
 //   bf16: there is no packed bf16 arithmetic on gfx950, so each value goes
-//         through fp32: fma(q, s, -z*s) is exact (|q - z| <= 15 has 4 bits, s
-//         has 8 significant bits, and -z*s is itself exact), then
-//         v_cvt_pk_bf16_f32 rounds once per value.  When -z*s overflows fp32
-//         (scales above about 2.3e37) the launch uses (q - z) * s instead,
-//         also exact before the one rounding (a flag in the blob trailer).
+//         through fp32.  The nibbles are unpacked with the same fp16 trick as
+//         above (1024+q or 64+q, exact), and one v_fma_mix_f32 per value reads
+//         that fp16 half straight from the packed register: fma(B+q, s,
+//         -(B+z)*s) is (q - z) * s exactly (B+z has at most 11 significant
+//         bits and s 8, so -(B+z)*s is exact in fp32, and so is the result),
+//         then v_cvt_pk_bf16_f32 rounds once per value.  When -(1024+z)*s
+//         overflows fp32 (scales above about 3.2e35) the launch uses
+//         (q - z) * s instead, also exact before the one rounding (a flag in
+//         the blob trailer).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -53,7 +57,8 @@ struct ColParams<DT_F16> {
 template <>
 struct ColParams<DT_BF16> {
     float s;       // the scale, exactly
-    float nzs;     // -z*s, exact in fp32 unless it overflows (then infinite)
+    float cA;      // -(1024+z)*s, exact in fp32 unless it overflows (then infinite)
+    float cB;      // -(64+z)*s, exact in fp32 when cA is finite
     float zneg;    // -z (used only by the exact form)
 };
 
@@ -70,7 +75,8 @@ __device__ __forceinline__ ColParams<DT_BF16> make_params(uint32_t sbits, uint32
                                                           ColParams<DT_BF16>*) {
     ColParams<DT_BF16> p;
     p.s = __uint_as_float(sbits << 16);
-    p.nzs = -((float)z * p.s);
+    p.cA = -((float)(1024u + z) * p.s);
+    p.cB = -((float)(64u + z) * p.s);
     p.zneg = -(float)z;
     return p;
 }
@@ -127,32 +133,29 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 __device__ __forceinline__ u32x4 dequant_word(uint32_t w, const ColParams<DT_BF16>& p) {
-    // Bytes of lo hold nibble positions 0,2,4,6 (j = 0,4,1,5); bytes of hi hold
-    // positions 1,3,5,7 (j = 2,6,3,7).  Byte -> fp32 is v_cvt_f32_ubyteN.
-    const uint32_t lo = opaque_v(w & 0x0F0F0F0Fu);
-    const uint32_t hi = opaque_v((w >> 4) & 0x0F0F0F0Fu);
-    const float j0 = __builtin_fmaf((float)(lo & 0xFFu), p.s, p.nzs);
-    const float j1 = __builtin_fmaf((float)((lo >> 16) & 0xFFu), p.s, p.nzs);
-    const float j2 = __builtin_fmaf((float)(hi & 0xFFu), p.s, p.nzs);
-    const float j3 = __builtin_fmaf((float)((hi >> 16) & 0xFFu), p.s, p.nzs);
-    const float j4 = __builtin_fmaf((float)((lo >> 8) & 0xFFu), p.s, p.nzs);
-    const float j5 = __builtin_fmaf((float)(lo >> 24), p.s, p.nzs);
-    const float j6 = __builtin_fmaf((float)((hi >> 8) & 0xFFu), p.s, p.nzs);
-    const float j7 = __builtin_fmaf((float)(hi >> 24), p.s, p.nzs);
+    // The same four (j, j+1) pairs as the fp16 form, each half widened inside
+    // the fma (v_fma_mix_f32): 1 shift, 4 v_and_or_b32, 8 fma, 4 cvt.
+    const uint32_t w8 = w >> 8;
+    const uint32_t gA = opaque_v(0x64006400u);   // fp16 1024 in both halves
+    const uint32_t gB = opaque_v(0x54005400u);   // fp16 64 in both halves
+    const f16x2 v0 = __builtin_bit_cast(f16x2, and_or(w, 0x000F000Fu, gA));    // 1024 + q
+    const f16x2 v1 = __builtin_bit_cast(f16x2, and_or(w, 0x00F000F0u, gB));    // 64 + q
+    const f16x2 v2 = __builtin_bit_cast(f16x2, and_or(w8, 0x000F000Fu, gA));
+    const f16x2 v3 = __builtin_bit_cast(f16x2, and_or(w8, 0x00F000F0u, gB));
     u32x4 r;
-    r.x = pack_bf16x2(j0, j1);
-    r.y = pack_bf16x2(j2, j3);
-    r.z = pack_bf16x2(j4, j5);
-    r.w = pack_bf16x2(j6, j7);
+    r.x = pack_bf16x2(__builtin_fmaf((float)v0.x, p.s, p.cA), __builtin_fmaf((float)v0.y, p.s, p.cA));
+    r.y = pack_bf16x2(__builtin_fmaf((float)v1.x, p.s, p.cB), __builtin_fmaf((float)v1.y, p.s, p.cB));
+    r.z = pack_bf16x2(__builtin_fmaf((float)v2.x, p.s, p.cA), __builtin_fmaf((float)v2.y, p.s, p.cA));
+    r.w = pack_bf16x2(__builtin_fmaf((float)v3.x, p.s, p.cB), __builtin_fmaf((float)v3.y, p.s, p.cB));
     return r;
 }
 
-// The fma form above needs -z*s to be exact; it overflows fp32 only for
-// scales beyond fp32_max/15 (about 2.3e37).  For such columns this form is
+// The fma form above needs -(1024+z)*s to be exact; it overflows fp32 only
+// for scales beyond fp32_max/1039 (about 3.2e35).  For such columns this form is
 // used instead: (q - z) exactly, then one product, then one RNE.
 __device__ __forceinline__ bool needs_exact_path(const ColParams<DT_F16>&) { return false; }
 __device__ __forceinline__ bool needs_exact_path(const ColParams<DT_BF16>& p) {
-    return __builtin_isinf(p.nzs);
+    return __builtin_isinf(p.cA);
 }
 
 __device__ __forceinline__ u32x4 dequant_word_exact(uint32_t w, const ColParams<DT_F16>& p) {

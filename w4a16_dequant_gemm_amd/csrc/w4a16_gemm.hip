@@ -465,12 +465,12 @@ __global__ __launch_bounds__(SK_WAVES * 64) void splitk_kernel(
 // ---------------------------------------------------------------------------
 constexpr int TK_WAVES = 8;
 
-template <int DT, bool SYM, int GS, int MT>
+template <int DT, bool SYM, int GS, int MT, bool FULL>
 __global__ __launch_bounds__(TK_WAVES * 64) void tiled_kernel(
     const uint16_t* __restrict__ X, const uint8_t* __restrict__ packed, uint16_t* __restrict__ Y,
     float* __restrict__ part, uint32_t* __restrict__ cnt, int M, int N, int K,
     int steps_per_split, int S, size_t s_off, size_t z_off, size_t t_off) {
-    constexpr int KT = 8;                       // k-steps per stage
+    constexpr int KT = kTiledStage;             // k-steps per stage
     constexpr int ROWS = 32 * MT;
     constexpr int CPR = 2 * KT;                 // 16-byte chunks per row and stage
     constexpr int SLOTS = ROWS * CPR;           // 16-byte slots per stage buffer
@@ -478,6 +478,7 @@ __global__ __launch_bounds__(TK_WAVES * 64) void tiled_kernel(
     constexpr int SPG = GS < KT ? GS : KT;      // k-steps per group inside a stage
     constexpr int NGST = KT / SPG;              // groups per stage
     static_assert(CPR == 16, "the swizzle assumes 16 chunks per row");
+    static_assert(2 * XI <= KT, "the activation copies of a stage fit in its k-steps");
     constexpr int NW = MT == 2 ? 3 : 2;         // stages in flight (LDS buffers, weight sets)
     __shared__ __align__(16) u32x4 xs0[SLOTS];
     __shared__ __align__(16) u32x4 xs1[SLOTS];
@@ -527,19 +528,16 @@ __global__ __launch_bounds__(TK_WAVES * 64) void tiled_kernel(
         const int st = s_beg + min(si, nst - 1) * KT;
         return min(kKStep * st + 8 * xchunk, K - 8);   // past K: never used
     };
-    auto load_x = [&](int si) {   // MT = 2: into xr
-        const int kk = x_col(si);
-#pragma unroll
-        for (int i = 0; i < (DMA ? 0 : XI); ++i) xr[i] = *(const u32x4*)(xrow[i] + kk);
+    // The loads of one stage come in parts, one call per k-step of the stage
+    // before, so that they interleave with its matrix instructions.
+    auto load_x_part = [&](int si, int i) {   // MT = 2: copy i into xr[i]
+        if constexpr (!DMA) xr[i] = *(const u32x4*)(xrow[i] + x_col(si));
     };
-    auto store_x = [&](u32x4* buf) {
-#pragma unroll
-        for (int i = 0; i < (DMA ? 0 : XI); ++i) buf[(TK_WAVES * i + wave) * 64 + lane] = xr[i];
+    auto store_x_part = [&](u32x4* buf, int i) {   // MT = 2
+        if constexpr (!DMA) buf[(TK_WAVES * i + wave) * 64 + lane] = xr[i];
     };
-    auto copy_x = [&](u32x4* buf, int si) {   // MT = 4: straight into LDS
-        const int kk = x_col(si);
-#pragma unroll
-        for (int i = 0; i < XI; ++i) load_to_lds16(xrow[i] + kk, &buf[(TK_WAVES * i + wave) * 64]);
+    auto copy_x_part = [&](u32x4* buf, int si, int i) {   // MT = 4: straight into LDS
+        load_to_lds16(xrow[i] + x_col(si), &buf[(TK_WAVES * i + wave) * 64]);
     };
 
     struct Stage {
@@ -547,17 +545,21 @@ __global__ __launch_bounds__(TK_WAVES * 64) void tiled_kernel(
         uint32_t zw[NGST];
         u32x2 w[KT];
     };
-    auto load_w = [&](Stage& b, int si) {
+    auto load_w_part = [&](Stage& b, int si, int u) {
         const int st = s_beg + min(si, nst - 1) * KT;
+        if (u == 0) {
 #pragma unroll
-        for (int j = 0; j < NGST; ++j) {
-            const int g = min(st + j * SPG, s_end - 1) / GS;
-            b.sc[j] = *(const uint32_t*)(srec + (size_t)g * kScaleRecBytes);
-            b.zw[j] = SYM ? 0u : (uint32_t)*(const uint16_t*)(zrec + (size_t)g * kZeroRecBytes);
+            for (int j = 0; j < NGST; ++j) {
+                const int g = min(st + j * SPG, s_end - 1) / GS;
+                b.sc[j] = *(const uint32_t*)(srec + (size_t)g * kScaleRecBytes);
+                b.zw[j] = SYM ? 0u : (uint32_t)*(const uint16_t*)(zrec + (size_t)g * kZeroRecBytes);
+            }
         }
+        b.w[u] = __builtin_nontemporal_load(wbase + (size_t)min(st + u, s_end - 1) * 128);
+    };
+    auto load_w = [&](Stage& b, int si) {
 #pragma unroll
-        for (int u = 0; u < KT; ++u)
-            b.w[u] = __builtin_nontemporal_load(wbase + (size_t)min(st + u, s_end - 1) * 128);
+        for (int u = 0; u < KT; ++u) load_w_part(b, si, u);
     };
 
     f32x16 acc[MT][2];
@@ -571,63 +573,83 @@ __global__ __launch_bounds__(TK_WAVES * 64) void tiled_kernel(
     // 2u ^ ((lane/32) ^ (lane & 15)).
     const int aswz = (lane >> 5) ^ (lane & 15);
     const int arow = (lane & 31) * CPR;
-    // issue_ahead() issues the loads of a later stage once this stage's
-    // first operands are in registers (so no wait for them can also wait for
-    // the younger loads).
-    auto compute = [&](const Stage& b, const u32x4* buf, int si, auto exact, auto issue_ahead) {
+    // One stage.  The operands of k-step 0 are prepared first; during k-step
+    // u the wave prepares those of k-step u+1 between its matrix
+    // instructions: while the MT MFMAs of column tile 0 run, tile 1's next
+    // weight word is dequantized into a spare register; while those of tile
+    // 1 run (tile 0's B operand is free by then), tile 0's next word, and the
+    // next A operands are read from LDS as each row tile's last MFMA has
+    // issued.  A wave hides a few vector instructions under each of its own
+    // MFMAs, and the other wave on the SIMD fills the rest.  issue(u) issues
+    // part u of a later stage's loads.
+    auto compute = [&](const Stage& b, const u32x4* buf, int si, auto exact, auto issue) {
         const int nvalid = min(KT, s_end - (s_beg + si * KT));   // <= 0 past the end
         auto read_a = [&](u32x4 (&a)[MT], int u) {
 #pragma unroll
             for (int r = 0; r < MT; ++r) a[r] = buf[arow + 32 * CPR * r + ((2 * u) ^ aswz)];
         };
-        auto make_b = [&](u32x4 (&bo)[2], int u) {
+        auto make_b1 = [&](int u, int tt) {
             const int j = u / SPG;
             const u32x2 sc2 = {b.sc[j], b.sc[j]};
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                const ColParams<DT> prm = tile_params<DT, SYM>(sc2, b.zw[j], 2 * half + tt);
-                bo[tt] = dequant_sel<decltype(exact)::value>(b.w[u][tt], prm);
-            }
+            const ColParams<DT> prm = tile_params<DT, SYM>(sc2, b.zw[j], 2 * half + tt);
+            return dequant_sel<decltype(exact)::value>(b.w[u][tt], prm);
         };
-        // MT = 2 prepares the next k-step's operands (A from LDS, B
-        // dequantized) before this k-step's MFMAs; MT = 4 has no registers for
-        // them and prepares each k-step's operands just before its MFMAs (the
-        // other wave on the SIMD runs meanwhile).
-        constexpr bool AHEAD = MT == 2;
+        if (FULL && nvalid <= 0) return;   // a stage past the last one: nothing to do
         u32x4 a[MT], bo[2];
         read_a(a, 0);
-        make_b(bo, 0);
-        if constexpr (DMA) __builtin_amdgcn_sched_barrier(0);   // keep the loads below
-        issue_ahead();
+        bo[0] = make_b1(0, 0);
+        bo[1] = make_b1(0, 1);
+        if constexpr (!FULL) {
+            // K not a multiple of the stage: the plain order, which stops after
+            // the last k-step of the split
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int u = 0; u < KT; ++u) {
-            if (u >= nvalid) break;
-            if constexpr (AHEAD) {
-                u32x4 an[MT], bn[2];
-                if (u + 1 < KT) {
-                    read_a(an, u + 1);
-                    make_b(bn, u + 1);
-                }
+            for (int u = 0; u < KT; ++u) issue(u);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                    for (int r = 0; r < MT; ++r) acc[r][tt] = mfma32x32x16<DT>(a[r], bo[tt], acc[r][tt]);
-                if (u + 1 < KT) {
-#pragma unroll
-                    for (int r = 0; r < MT; ++r) a[r] = an[r];
-#pragma unroll
-                    for (int tt = 0; tt < 2; ++tt) bo[tt] = bn[tt];
-                }
-            } else {
+            for (int u = 0; u < KT; ++u) {
+                if (u >= nvalid) break;
                 if (u > 0) {
                     read_a(a, u);
-                    make_b(bo, u);
+                    bo[0] = make_b1(u, 0);
+                    bo[1] = make_b1(u, 1);
                 }
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
                     for (int r = 0; r < MT; ++r) acc[r][tt] = mfma32x32x16<DT>(a[r], bo[tt], acc[r][tt]);
             }
+        } else {
+#pragma unroll
+            for (int u = 0; u < KT; ++u) {
+                __builtin_amdgcn_sched_barrier(0);
+                issue(u);
+                const bool nx = u + 1 < KT;
+                u32x4 bn1;
+#pragma unroll
+                for (int r = 0; r < MT; ++r) acc[r][0] = mfma32x32x16<DT>(a[r], bo[0], acc[r][0]);
+                if (nx) bn1 = make_b1(u + 1, 1);
+#pragma unroll
+                for (int r = 0; r < MT; ++r) acc[r][1] = mfma32x32x16<DT>(a[r], bo[1], acc[r][1]);
+                if (nx) {
+                    bo[0] = make_b1(u + 1, 0);
+                    read_a(a, u + 1);
+                    bo[1] = bn1;
+                }
+                // MFMA / vector ALU / LDS-read interleave of this k-step
+#pragma unroll
+                for (int r = 0; r < MT; ++r) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 20 / MT, 0);
+                }
+#pragma unroll
+                for (int r = 0; r < MT; ++r) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 20 / MT, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
@@ -644,32 +666,50 @@ __global__ __launch_bounds__(TK_WAVES * 64) void tiled_kernel(
     auto mainloop = [&](auto exact) {
         if constexpr (NW == 3) {
             Stage A, B, C;
-            load_x(0);
+#pragma unroll
+            for (int i = 0; i < XI; ++i) load_x_part(0, i);
             load_w(A, 0);
             load_w(B, 1);
-            store_x(xs0);
-            load_x(1);
+#pragma unroll
+            for (int i = 0; i < XI; ++i) store_x_part(xs0, i);
+#pragma unroll
+            for (int i = 0; i < XI; ++i) load_x_part(1, i);
             stage_barrier_lds();
+            // during stage i: the activations of stage i+1 (in xr) go to LDS
+            // at k-steps 0..XI-1, those of stage i+2 are loaded into xr at
+            // k-steps XI..2XI-1, the weights of stage i+2 one k-step at a time
+            auto part = [&](u32x4* to, int si, Stage& w, int u) {
+                if (u < XI) store_x_part(to, u);
+                else if (u < 2 * XI) load_x_part(si, u - XI);
+                load_w_part(w, si, u);
+            };
             int i = 0;
             do {
-                compute(A, xs0, i, exact, [&] { store_x(xs1); load_x(i + 2); load_w(C, i + 2); });
+                compute(A, xs0, i, exact, [&](int u) { part(xs1, i + 2, C, u); });
                 stage_barrier_lds();
-                compute(B, xs1, i + 1, exact, [&] { store_x(xs2); load_x(i + 3); load_w(A, i + 3); });
+                compute(B, xs1, i + 1, exact, [&](int u) { part(xs2, i + 3, A, u); });
                 stage_barrier_lds();
-                compute(C, xs2, i + 2, exact, [&] { store_x(xs0); load_x(i + 4); load_w(B, i + 4); });
+                compute(C, xs2, i + 2, exact, [&](int u) { part(xs0, i + 4, B, u); });
                 stage_barrier_lds();
                 i += 3;
             } while (i < nst);
         } else {
             Stage A, B;
-            copy_x(xs0, 0);
+#pragma unroll
+            for (int i = 0; i < XI; ++i) copy_x_part(xs0, 0, i);
             load_w(A, 0);
             stage_barrier_all();
+            // during stage i: stage i+1's activations are copied into LDS at
+            // k-steps 0..XI-1 and its weights loaded one k-step at a time
+            auto part = [&](u32x4* to, int si, Stage& w, int u) {
+                if (u < XI) copy_x_part(to, si, u);
+                load_w_part(w, si, u);
+            };
             int i = 0;
             do {
-                compute(A, xs0, i, exact, [&] { copy_x(xs1, i + 1); load_w(B, i + 1); });
+                compute(A, xs0, i, exact, [&](int u) { part(xs1, i + 1, B, u); });
                 stage_barrier_all();
-                compute(B, xs1, i + 1, exact, [&] { copy_x(xs0, i + 2); load_w(A, i + 2); });
+                compute(B, xs1, i + 1, exact, [&](int u) { part(xs0, i + 2, A, u); });
                 stage_barrier_all();
                 i += 2;
             } while (i < nst);
@@ -780,20 +820,28 @@ void launch_splitk(const void* X, const void* packed, void* Y, int64_t M, const 
     else launch_splitk_mb<DT, SYM, GS, 32>(X, packed, Y, M, L, p, part, cnt, stream);
 }
 
+template <int DT, bool SYM, int GS, int MT, bool FULL>
+void launch_tiled_mt(const void* X, const void* packed, void* Y, int64_t M, const Layout& L,
+                     const Plan& p, float* part, uint32_t* cnt, hipStream_t stream) {
+    hipLaunchKernelGGL((tiled_kernel<DT, SYM, GS, MT, FULL>), dim3(p.grid_x, p.grid_y, p.grid_z),
+                       dim3(TK_WAVES * 64), 0, stream, (const uint16_t*)X, (const uint8_t*)packed,
+                       (uint16_t*)Y, part, cnt, (int)M, (int)L.N, (int)L.K, p.steps_per_split,
+                       p.splits, L.s_off, L.z_off, L.t_off);
+}
+
+// FULL: every stage of every split has all its k-steps (K a multiple of the
+// stage depth, 128), which the interleaved schedule assumes.
 template <int DT, bool SYM, int GS>
 void launch_tiled(const void* X, const void* packed, void* Y, int64_t M, const Layout& L,
                   const Plan& p, float* part, uint32_t* cnt, hipStream_t stream) {
-    const dim3 grid(p.grid_x, p.grid_y, p.grid_z), block(TK_WAVES * 64);
-    if (p.mt == 2)
-        hipLaunchKernelGGL((tiled_kernel<DT, SYM, GS, 2>), grid, block, 0, stream,
-                           (const uint16_t*)X, (const uint8_t*)packed, (uint16_t*)Y, part, cnt,
-                           (int)M, (int)L.N, (int)L.K, p.steps_per_split, p.splits, L.s_off,
-                           L.z_off, L.t_off);
-    else
-        hipLaunchKernelGGL((tiled_kernel<DT, SYM, GS, 4>), grid, block, 0, stream,
-                           (const uint16_t*)X, (const uint8_t*)packed, (uint16_t*)Y, part, cnt,
-                           (int)M, (int)L.N, (int)L.K, p.steps_per_split, p.splits, L.s_off,
-                           L.z_off, L.t_off);
+    const bool full = (L.K / kKStep) % kTiledStage == 0;
+    if (p.mt == 2) {
+        if (full) launch_tiled_mt<DT, SYM, GS, 2, true>(X, packed, Y, M, L, p, part, cnt, stream);
+        else launch_tiled_mt<DT, SYM, GS, 2, false>(X, packed, Y, M, L, p, part, cnt, stream);
+    } else {
+        if (full) launch_tiled_mt<DT, SYM, GS, 4, true>(X, packed, Y, M, L, p, part, cnt, stream);
+        else launch_tiled_mt<DT, SYM, GS, 4, false>(X, packed, Y, M, L, p, part, cnt, stream);
+    }
 }
 
 template <int DT, bool SYM>

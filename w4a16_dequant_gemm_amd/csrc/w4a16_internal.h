@@ -14,6 +14,7 @@ enum Variant { VARIANT_SPLITK = 0, VARIANT_TILED = 1 };
 // Split-K kernel geometry, shared by the plan and the kernel.
 constexpr int kSplitKWaves = 8;   // waves per workgroup (two per SIMD), one workgroup per CU
 constexpr int kSplitKBatch = 4;   // k-steps per batch
+constexpr int kTiledStage = 8;    // k-steps per stage of the tiled kernel (128 of K)
 
 // How one w4a16_gemm call is executed.  Computed on the host from the shape
 // only, so w4a16_workspace_bytes and w4a16_gemm always agree.
