@@ -100,6 +100,10 @@ __device__ __forceinline__ bool uses_exact_form(const uint8_t* packed, size_t t_
 // A seq_cst __threadfence() here would write back and invalidate a whole
 // XCD's L2 per workgroup, which costs far more than the GEMM itself.
 // ---------------------------------------------------------------------------
+// Buffer resource word 3 for raw (untyped) buffer accesses, and the cache
+// policy bit of device-scope accesses (sc1), as used by the atomics below.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+constexpr int kDeviceScope = 16;
 __device__ __forceinline__ void st_dev(float* p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -478,7 +482,7 @@ __global__ __launch_bounds__(TK_WAVES * 64) void tiled_kernel(
     constexpr int SPG = GS < KT ? GS : KT;      // k-steps per group inside a stage
     constexpr int NGST = KT / SPG;              // groups per stage
     static_assert(CPR == 16, "the swizzle assumes 16 chunks per row");
-    static_assert(2 * XI <= KT, "the activation copies of a stage fit in its k-steps");
+    static_assert(2 * XI <= KT, "the activation copies of a stage fit in its first half");
     constexpr int NW = MT == 2 ? 3 : 2;         // stages in flight (LDS buffers, weight sets)
     __shared__ __align__(16) u32x4 xs0[SLOTS];
     __shared__ __align__(16) u32x4 xs1[SLOTS];
@@ -675,13 +679,22 @@ __global__ __launch_bounds__(TK_WAVES * 64) void tiled_kernel(
 #pragma unroll
             for (int i = 0; i < XI; ++i) load_x_part(1, i);
             stage_barrier_lds();
-            // during stage i: the activations of stage i+1 (in xr) go to LDS
-            // at k-steps 0..XI-1, those of stage i+2 are loaded into xr at
-            // k-steps XI..2XI-1, the weights of stage i+2 one k-step at a time
+            // during stage i: at k-step 0 the activations of stage i+1 (in xr
+            // since k-step 0 of stage i-1) go to LDS and those of stage i+2 are
+            // loaded into xr -- first, so that waiting for them never waits
+            // for the weight loads after them; the weights of stage i+2 two
+            // k-steps at a time in the first half of the stage
             auto part = [&](u32x4* to, int si, Stage& w, int u) {
-                if (u < XI) store_x_part(to, u);
-                else if (u < 2 * XI) load_x_part(si, u - XI);
-                load_w_part(w, si, u);
+                if (u == 0) {
+#pragma unroll
+                    for (int i = 0; i < XI; ++i) store_x_part(to, i);
+#pragma unroll
+                    for (int i = 0; i < XI; ++i) load_x_part(si, i);
+                }
+                if (2 * u < KT) {
+                    load_w_part(w, si, 2 * u);
+                    load_w_part(w, si, 2 * u + 1);
+                }
             };
             int i = 0;
             do {
@@ -699,11 +712,16 @@ __global__ __launch_bounds__(TK_WAVES * 64) void tiled_kernel(
             for (int i = 0; i < XI; ++i) copy_x_part(xs0, 0, i);
             load_w(A, 0);
             stage_barrier_all();
-            // during stage i: stage i+1's activations are copied into LDS at
-            // k-steps 0..XI-1 and its weights loaded one k-step at a time
+            // during stage i: stage i+1's activations are copied into LDS and
+            // its weights loaded in the first half of the stage (one copy and
+            // two weight loads per k-step), so that all of them have the
+            // second half to arrive before the barrier that ends the stage
             auto part = [&](u32x4* to, int si, Stage& w, int u) {
                 if (u < XI) copy_x_part(to, si, u);
-                load_w_part(w, si, u);
+                if (2 * u < KT) {
+                    load_w_part(w, si, 2 * u);
+                    load_w_part(w, si, 2 * u + 1);
+                }
             };
             int i = 0;
             do {
@@ -738,43 +756,67 @@ __global__ __launch_bounds__(TK_WAVES * 64) void tiled_kernel(
         return;
     }
 
-    // Cross-workgroup reduction; slot float index
-    // (((wave*MT + r)*2 + tt)*16 + i)*64 + lane.
+    // Cross-workgroup reduction.  A split's partial tile is Q chunks of four
+    // accumulator registers per lane, chunk q of wave w at 16-byte slot
+    // (w*Q + q)*64 + lane: each store and load instruction of a wave moves
+    // 1 KiB, through device-scope (sc1) buffer accesses.
     const int tile = blockIdx.y * gridDim.x + blockIdx.x;
-    constexpr int RPW = MT * 2 * 16;   // accumulator registers per lane
-    const size_t slot_floats = (size_t)TK_WAVES * RPW * 64;
-    float* base = part + (size_t)tile * S * slot_floats + (size_t)wave * RPW * 64 + lane;
-    {
-        float* mine = base + (size_t)split * slot_floats;
+    constexpr int Q = MT * 2 * 4;                               // chunks per lane
+    constexpr uint32_t slot_bytes = TK_WAVES * Q * 64 * 16;    // one split's tile
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        part + (size_t)tile * S * (slot_bytes / 4), (short)0, (int)(S * slot_bytes), kBufferRsrcWord3);
+    const uint32_t lane_off = ((uint32_t)wave * Q * 64 + lane) * 16;
+    auto chunk = [&](int q) {   // registers 4j..4j+3 of tile (r, tt), q = (2r + tt)*4 + j
+        const f32x16& c = acc[q >> 3][(q >> 2) & 1];
+        const int j = q & 3;
+        return f32x4{c[4 * j], c[4 * j + 1], c[4 * j + 2], c[4 * j + 3]};
+    };
 #pragma unroll
-        for (int r = 0; r < MT; ++r)
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) st_dev(&mine[((r * 2 + tt) * 16 + i) * 64], acc[r][tt][i]);
-    }
+    for (int q = 0; q < Q; ++q)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, chunk(q)), rs,
+                                               (int)(split * slot_bytes + lane_off + q * 1024), 0,
+                                               kDeviceScope);
     if (!arrive_last(&cnt[tile], S, &s_last)) return;
 
-    // Sum the S slots in split order 0..S-1, one 32x32 tile at a time (this
-    // workgroup's own slot is read back too, so every tile is summed the same
-    // way whichever workgroup is last).
-#pragma unroll 1
-    for (int rt = 0; rt < MT * 2; ++rt) {
-        const int r = rt >> 1;
-        const int tt = rt & 1;
-        float v[16];
+    // Sum the S partials in split order 0..S-1 (this workgroup's own from its
+    // registers, the same values that it stored), QG chunks at a time, with
+    // the loads of up to SB splits in flight together.
+    constexpr int QG = 4, SB = 4;
+    auto load_chunk = [&](int sp, int q) {
+        return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             rs, (int)(sp * slot_bytes + lane_off + q * 1024), 0,
+                                             kDeviceScope));
+    };
 #pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = ld_dev(&base[(rt * 16 + i) * 64]);
-        for (int s = 1; s < S; ++s) {
-            const float* src = base + (size_t)s * slot_floats;
+    for (int q0 = 0; q0 < Q; q0 += QG) {
+        f32x4 v[QG];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) v[i] += ld_dev(&src[(rt * 16 + i) * 64]);
+        for (int g = 0; g < QG; ++g) v[g] = split == 0 ? chunk(q0 + g) : load_chunk(0, q0 + g);
+        for (int s0 = 1; s0 < S; s0 += SB) {
+            f32x4 t[SB][QG];
+#pragma unroll
+            for (int k = 0; k < SB; ++k) {
+                const int sp = min(s0 + k, S - 1);
+#pragma unroll
+                for (int g = 0; g < QG; ++g) t[k][g] = sp == split ? chunk(q0 + g) : load_chunk(sp, q0 + g);
+            }
+#pragma unroll
+            for (int k = 0; k < SB; ++k)
+                if (s0 + k < S) {
+#pragma unroll
+                    for (int g = 0; g < QG; ++g) v[g] += t[k][g];
+                }
         }
         if (nb_ok) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int rr = m0 + 32 * r + acc_row(i, lane);
-                if (rr < M) Y[(int64_t)rr * N + colw + 32 * tt] = round_out<DT>(v[i]);
+            for (int g = 0; g < QG; ++g) {
+                const int q = q0 + g;
+                const int r = q >> 3, tt = (q >> 2) & 1, j = q & 3;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int rr = m0 + 32 * r + acc_row(4 * j + e, lane);
+                    if (rr < M) Y[(int64_t)rr * N + colw + 32 * tt] = round_out<DT>(v[g][e]);
+                }
             }
         }
     }
