@@ -13,8 +13,8 @@
 //  * splitk_kernel (M <= 32).  Memory-bound streaming.  The weight chunks
 //    (one 1 KiB chunk per k-step of a 128-column block) are dealt out in equal
 //    contiguous ranges to every wave of the grid; each lane issues one
-//    16-byte load per k-step, and each wave keeps two 4-k-step batches in
-//    flight while it computes a third.  The activation rows come straight
+//    16-byte load per k-step, and each wave keeps the next 4-k-step batch in
+//    flight while it computes the current one.  The activation rows come straight
 //    from global memory (they are tiny and L2-resident).  Partial sums of a
 //    column block split between waves are reduced through LDS and between
 //    workgroups through a workspace, both in a fixed order.  The
@@ -137,10 +137,12 @@ __device__ __forceinline__ void reset_counter(uint32_t* counter) {
 // ranges to every wave of the grid (one workgroup of SK_WAVES waves per CU,
 // two waves per SIMD so that one wave's dequantization overlaps the other's
 // matrix instructions).  A wave streams its range as one continuous
-// pipeline: while it computes batch b, batches b+1 and b+2 (weights, their
-// scale/zero records and the activation operands) are in flight in
-// registers, across column-block boundaries.  No barrier and no LDS traffic
-// in the main loop.
+// pipeline: while it computes batch b, batch b+1 (weights, their scale/zero
+// records and the activation operands) is in flight in registers, across
+// column-block boundaries.  No barrier and no LDS traffic in the main loop.
+// (Measured on MI355X: one batch ahead beats two or three -- with 16 waves'
+// worth of loads per CU in flight the memory system is kept busy, and the
+// smaller register footprint and loop body win over the deeper prefetch.)
 //
 // Where the range leaves a column block, a block the wave covered entirely
 // is written to Y; the wave's first block, if partial, goes to the wave's LDS
@@ -155,7 +157,7 @@ __device__ __forceinline__ void reset_counter(uint32_t* counter) {
 // ---------------------------------------------------------------------------
 constexpr int SK_WAVES = kSplitKWaves;
 constexpr int SK_U = kSplitKBatch;
-constexpr int SK_NBUF = 3;   // batches held in registers per wave
+constexpr int SK_NBUF = 2;   // batches held in registers per wave
 
 // Balanced contiguous split of TB batches over the grid's waves: wave gw
 // starts at gw*base + min(gw, rem) and owns base (+1 if gw < rem) batches.
