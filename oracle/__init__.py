@@ -66,6 +66,8 @@ def _load():
     lib.oracle_gemm.restype = ci
     lib.oracle_gemm_at.argtypes = [p, p, p, p, i64, i64, i64, i64, ci, ci, p, p, i64, p, p, ci]
     lib.oracle_gemm_at.restype = ci
+    lib.oracle_epilogue.argtypes = [p, p, p, p, i64, i64, i64, p, p, p, ci, ci, ci, p, p]
+    lib.oracle_epilogue.restype = ci
     _lib = lib
     return lib
 
@@ -172,6 +174,40 @@ def gemm_at(X, qweight, scales, zeros, M, N, K, G, dtype, sym, ms, ns, nthreads=
     if rc:
         raise ValueError(f"oracle_gemm_at failed with status {rc}")
     return Y, B
+
+
+ACTIVATIONS = {"none": 0, "relu": 1, "silu": 2}
+AUX_OPS = {"add": 0, "mul": 1}
+
+
+def epilogue(Y, B, M, N, dtype, col_scale=None, bias=None, aux=None, activation="none",
+             aux_op="add", ms=None, ns=None):
+    """(Yo, Bo): the epilogue y = aux_op(act(Y*c + b), a) and its error-bound
+    denominator, in fp64.  Y, B are [M][N] (full output) or, with ms/ns, the
+    sampled elements (ms[i], ns[i]).  col_scale: float values [N]; bias: bit
+    patterns [N]; aux: bit patterns [M][N]; each optional."""
+    Yf = np.ascontiguousarray(np.asarray(Y, dtype=np.float64).ravel())
+    Bf = np.ascontiguousarray(np.asarray(B, dtype=np.float64).ravel())
+    if ms is None:
+        mm, nn = np.meshgrid(np.arange(M, dtype=np.int64), np.arange(N, dtype=np.int64),
+                             indexing="ij")
+        ms, ns = mm.ravel(), nn.ravel()
+    ms = _c(ms, np.int64).ravel()
+    ns = _c(ns, np.int64).ravel()
+    assert ms.size == ns.size == Yf.size == Bf.size
+    cs = None if col_scale is None else _c(np.asarray(col_scale, dtype=np.float64).ravel(), np.float64)
+    bs = None if bias is None else _c(bias, np.uint16)
+    ax = None if aux is None else _c(aux, np.uint16)
+    Yo = np.empty_like(Yf)
+    Bo = np.empty_like(Bf)
+    code = dtype_code(dtype) if isinstance(dtype, str) else dtype
+    rc = _load().oracle_epilogue(_ptr(Yf), _ptr(Bf), _ptr(ms), _ptr(ns), ms.size, M, N,
+                                 _ptr(cs), _ptr(bs), _ptr(ax), code, ACTIVATIONS[activation],
+                                 AUX_OPS[aux_op], _ptr(Yo), _ptr(Bo))
+    if rc:
+        raise ValueError(f"oracle_epilogue failed with status {rc}")
+    shape = np.shape(Y)
+    return Yo.reshape(shape), Bo.reshape(shape)
 
 
 def bits_to_float(bits: np.ndarray, dtype) -> np.ndarray:

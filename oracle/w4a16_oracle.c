@@ -36,6 +36,19 @@
  * Every product X*deq is exact in fp64 (11+11 significant bits at most), so
  * Y differs from the exact rational sum by at most about K * 2^-53 * B.
  *
+ * Epilogue (oracle_epilogue), the output-side steps the fused kernel may run
+ * before its single store.  Page "量化开销对比", sections 6.2 (after the k
+ * loop the accumulator is multiplied by a scale, the bias is added and the
+ * result written), 6.6 (dequant, GEMM, scale and bias, plus residual or
+ * activation, in one kernel) and 6.7 (a per-channel scale multiplies the
+ * output in the epilogue).  Read, in this order, each step optional:
+ *   t = Y[m][n] * c[n] + b[n];   u = act(t);   y = u + a[m][n]  or  u * a[m][n]
+ * with act = identity, ReLU max(t, 0) or SiLU t / (1 + exp(-t)), all in fp64.
+ * Its error-bound denominator carries B through the same steps:
+ *   Bo = |a| * L * (|c| * B + |b|)  (multiply)  or  L * (|c| * B + |b|) + |a|  (add),
+ * L = 1 (identity, ReLU) or 1.1 (SiLU, whose slope stays below 1.1), so that
+ * |y| <= Bo and the identity epilogue gives Bo = B.
+ *
  * Layouts (all row-major, the canonical tensors of the library boundary):
  *   X        uint16 bit patterns [M][K] (fp16 or bf16)
  *   qweight  uint32 [K/8][N]
@@ -408,4 +421,51 @@ int oracle_gemm_at(const uint16_t *X, const uint32_t *qweight, const uint16_t *s
         jobs[t] = j;
     }
     return run_jobs(jobs, nt, gemm_pairs);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Epilogue on n_el output elements (ms[i], ns[i]) of an M x N output:      */
+/* Y, B hold the accumulator and its bound for those elements (as returned  */
+/* by oracle_gemm or oracle_gemm_at).  col_scale: fp64 [N] or NULL; bias:   */
+/* bit patterns [N] or NULL; aux: bit patterns [M][N] or NULL.              */
+/* act: 0 identity, 1 ReLU, 2 SiLU.  aux_op: 0 add, 1 multiply.             */
+/* ------------------------------------------------------------------------ */
+static double act_apply(double t, int act)
+{
+    if (act == 1) return t > 0.0 ? t : 0.0;
+    if (act == 2) return t / (1.0 + exp(-t));
+    return t;
+}
+
+int oracle_epilogue(const double *Y, const double *B, const int64_t *ms, const int64_t *ns,
+                    int64_t n_el, int64_t M, int64_t N, const double *col_scale,
+                    const uint16_t *bias, const uint16_t *aux, int dtype, int act, int aux_op,
+                    double *Yout, double *Bout)
+{
+    if (dtype != ORACLE_F16 && dtype != ORACLE_BF16) return 1;
+    if (act < 0 || act > 2 || aux_op < 0 || aux_op > 1) return 1;
+    const double L = act == 2 ? 1.1 : 1.0;
+    for (int64_t i = 0; i < n_el; ++i) {
+        const int64_t m = ms[i], n = ns[i];
+        if (m < 0 || m >= M || n < 0 || n >= N) return 1;
+        const double c = col_scale ? col_scale[n] : 1.0;
+        const double b = bias ? to_double(bias[n], dtype) : 0.0;
+        double t = Y[i] * c + b;
+        double bt = fabs(c) * B[i] + fabs(b);
+        double y = act_apply(t, act);
+        double by = L * bt;
+        if (aux) {
+            const double a = to_double(aux[m * N + n], dtype);
+            if (aux_op == 1) {
+                y = y * a;
+                by = fabs(a) * by;
+            } else {
+                y = y + a;
+                by = by + fabs(a);
+            }
+        }
+        Yout[i] = y;
+        Bout[i] = by;
+    }
+    return 0;
 }
