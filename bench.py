@@ -291,13 +291,113 @@ def comparator_times(p, X, blobs, copies, stream, reps=20):
     return res
 
 
+LAYER_PREFIX = "ffn_layer_"
+LAYER_WORKLOADS = {f"ffn_layer_decode_m{m}_h8192_f28672_fp16_asym_g128": dict(M=m, H=8192, F=28672)
+                   for m in (1, 8)}
+
+
+def run_ffn_layer(name, steps, warmup, rotate_bytes=1 << 30):
+    """A decoder FFN block of a 70B-class model on the W4A16 path, the three
+    GEMMs with their epilogues fused and the launches captured in one HIP graph:
+        G = silu(X Wg);  H = (X Wu) * G;  Y = H Wd + X  (residual)
+    against the same GEMMs without epilogues followed by separate elementwise
+    launches (silu, multiply, add).  Weights rotate over cold copies."""
+    import torch
+
+    import w4a16_dequant_gemm_amd as w4
+
+    cfg = LAYER_WORKLOADS[name]
+    M, H, F, G = cfg["M"], cfg["H"], cfg["F"], 128
+    dev = torch.device("cuda:0")
+    flags = w4.flags_of("fp16", False)
+
+    def packed_of(K, N, seed):
+        qw, sc, zr, _ = synth.make_weights(K, N, G, "fp16", False, seed=seed)
+        t = w4.to_device(synth.Problem(1, K, N, G, "fp16", False, np.zeros((1, K), np.uint16),
+                                       qw, sc, zr), dev)
+        return w4.w4a16_repack(t[1], t[2], t[3], K, N, G, flags)
+
+    base = [packed_of(H, F, 11), packed_of(H, F, 12), packed_of(F, H, 13)]
+    layer_bytes = sum(b.data.numel() for b in base)
+    copies = max(2, min(8, math.ceil(rotate_bytes / layer_bytes)))
+    sets = [base] + [[w4.PackedW4(b.data.clone(), b.K, b.N, b.group_size, b.flags,
+                                  b.layout_version) for b in base] for _ in range(copies - 1)]
+    X = torch.from_numpy(synth.make_activations(M, H, "fp16", seed=0).view("int16")).view(
+        torch.float16).to(dev)
+    Gt = torch.empty((M, F), dtype=torch.float16, device=dev)
+    Ht = torch.empty_like(Gt)
+    Y = torch.empty((M, H), dtype=torch.float16, device=dev)
+    U = torch.empty_like(Gt)
+    ws = w4.workspace_for(max(w4.w4a16_workspace_bytes(M, F, H, G, flags),
+                              w4.w4a16_workspace_bytes(M, H, F, G, flags)), dev)
+    stream = torch.cuda.current_stream()
+
+    def fused(i):
+        wg, wu, wd = sets[i % copies]
+        w4.w4a16_gemm_ex(X, wg, Y=Gt, workspace=ws, activation="silu")
+        w4.w4a16_gemm_ex(X, wu, Y=Ht, workspace=ws, aux=Gt, aux_op="mul")
+        w4.w4a16_gemm_ex(Ht, wd, Y=Y, workspace=ws, aux=X, aux_op="add")
+
+    def unfused(i):
+        wg, wu, wd = sets[i % copies]
+        w4.w4a16_gemm(X, wg, Y=Gt, workspace=ws)
+        torch.nn.functional.silu(Gt, inplace=True)
+        w4.w4a16_gemm(X, wu, Y=U, workspace=ws)
+        torch.mul(U, Gt, out=Ht)
+        w4.w4a16_gemm(Ht, wd, Y=Y, workspace=ws)
+        Y.add_(X)
+
+    def graph_time(fn):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                fn(i)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        del g
+        return a.elapsed_time(b) / steps
+
+    ms_fused = graph_time(fused)
+    Yf = Y.clone()
+    ms_unfused = graph_time(unfused)
+    torch.cuda.synchronize()
+    diff = float((Yf.float() - Y.float()).abs().max())
+    nbytes = layer_bytes + (M * H * 2) * 3 + (M * F * 2) * 3   # weights, X, Y, G, H traffic
+    return {
+        "metric": "W4A16 FFN layer (3 fused GEMMs, one HIP graph) achieved HBM GB/s",
+        "value": round(nbytes / (ms_fused * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": steps, "warmup": warmup, "ms_per_step": round(ms_fused, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": name, "M": M, "hidden": H, "ffn": F, "group_size": G,
+                   "act_dtype": "fp16", "quant": "asym", "cold_weight_copies": copies,
+                   "launch": "hip_graph_replay"},
+        "layer_us_fused": round(ms_fused * 1e3, 3),
+        "layer_us_unfused_six_launches": round(ms_unfused * 1e3, 3),
+        "launches_fused": 3, "launches_unfused": 6,
+        "algorithmic_bytes": nbytes,
+        "max_abs_diff_fused_vs_unfused": diff,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
-                    help="a name from w4a16_synth.WORKLOADS, or 'all' (one line each)")
+                    help="a name from w4a16_synth.WORKLOADS, 'all' (one line each), or "
+                         "one of " + ", ".join(LAYER_WORKLOADS) + " (fused FFN block)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-comparators", action="store_true")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -317,6 +417,9 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.workload.startswith(LAYER_PREFIX):
+        print(json.dumps(run_ffn_layer(args.workload, args.steps, args.warmup)), flush=True)
+        return
     names = list(synth.WORKLOADS) if args.workload == "all" else [args.workload]
     for name in names:
         out = run_workload(name, args.steps, args.warmup,

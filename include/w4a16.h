@@ -141,6 +141,51 @@ w4a16_status_t w4a16_gemm(const void *X, const void *packed, size_t packed_bytes
                           int64_t M, int64_t N, int64_t K, int group_size, uint32_t flags,
                           void *workspace, size_t workspace_bytes, void *stream);
 
+/* Activations and auxiliary-operand combinations of the output epilogue. */
+#define W4A16_ACT_NONE 0
+#define W4A16_ACT_RELU 1
+#define W4A16_ACT_SILU 2
+#define W4A16_AUX_ADD 0
+#define W4A16_AUX_MUL 1
+
+/*
+ * Output epilogue of w4a16_gemm_ex.  Page "量化开销对比", sections 6.2, 6.6
+ * and 6.7: the per-channel scale, the bias and a residual or activation are
+ * applied to the accumulator inside the GEMM kernel, before its single store,
+ * instead of in further launches that re-read Y.  For output element (m, n),
+ * with v the fp32 accumulator, in this order and each step optional:
+ *   t = v * col_scale[n] + bias[n];   u = act(t);
+ *   y = u + aux[m][n]  (aux_op ADD)  or  u * aux[m][n]  (aux_op MUL);
+ *   Y[m][n] = y rounded to nearest even into the activation dtype.
+ * act: NONE (identity), RELU (max(t, 0)) or SILU (t / (1 + exp(-t))).  All
+ * arithmetic is fp32.  The struct is read on the host during the call only.
+ *
+ *   col_scale  dev, fp32 [N], 4-byte aligned, or NULL (no scale).
+ *   bias       dev, [N] in the activation dtype, 2-byte aligned, or NULL.
+ *   aux        dev, [M][N] row-major in the activation dtype, 2-byte aligned,
+ *              or NULL.  It may be Y itself (an in-place residual add) but
+ *              must not otherwise overlap Y.
+ *   activation W4A16_ACT_*.   aux_op  W4A16_AUX_* (ignored when aux is NULL).
+ */
+typedef struct {
+    const float *col_scale;
+    const void *bias;
+    const void *aux;
+    int32_t activation;
+    int32_t aux_op;
+} w4a16_epilogue_t;
+
+/*
+ * w4a16_gemm with an output epilogue (see w4a16_epilogue_t): the same
+ * arguments, kernels, workspace rules and errors, plus INVALID_ARG for an
+ * unknown activation or aux_op, a misaligned epilogue pointer, or an aux that
+ * partly overlaps Y.  epilogue == NULL is exactly w4a16_gemm.
+ */
+w4a16_status_t w4a16_gemm_ex(const void *X, const void *packed, size_t packed_bytes, void *Y,
+                             int64_t M, int64_t N, int64_t K, int group_size, uint32_t flags,
+                             const w4a16_epilogue_t *epilogue, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
 /*
  * Test and export aid: writes deq[K][N] row-major (activation dtype) from a
  * blob, using the same device dequantization code as w4a16_gemm.  This is the

@@ -34,7 +34,7 @@ W4A16_SYM = 0x2
 C_FUNCTIONS = (
     "w4a16_abi_version", "w4a16_layout_version", "w4a16_status_string", "w4a16_packed_bytes",
     "w4a16_repack", "w4a16_unrepack", "w4a16_workspace_bytes", "w4a16_gemm", "w4a16_dequant",
-    "w4a16_mfma_layout_probe",
+    "w4a16_mfma_layout_probe", "w4a16_gemm_ex",
 )
 
 
@@ -43,6 +43,16 @@ class W4A16Error(RuntimeError):
         self.status = status
         super().__init__(f"{where}: {status_string(status)} (status {status})")
 
+
+class Epilogue(ctypes.Structure):
+    """w4a16_epilogue_t of include/w4a16.h."""
+    _fields_ = [("col_scale", ctypes.c_void_p), ("bias", ctypes.c_void_p),
+                ("aux", ctypes.c_void_p), ("activation", ctypes.c_int32),
+                ("aux_op", ctypes.c_int32)]
+
+
+W4A16_ACT = {"none": 0, "relu": 1, "silu": 2}
+W4A16_AUX = {"add": 0, "mul": 1}
 
 _lib = None
 _layout_version = None
@@ -74,6 +84,9 @@ def load_library(path: str = LIB_PATH):
     lib.w4a16_workspace_bytes.restype = sz
     lib.w4a16_gemm.argtypes = [p, p, sz, p, i64, i64, i64, ci, u32, p, sz, p]
     lib.w4a16_gemm.restype = ci
+    lib.w4a16_gemm_ex.argtypes = [p, p, sz, p, i64, i64, i64, ci, u32, ctypes.POINTER(Epilogue), p,
+                                  sz, p]
+    lib.w4a16_gemm_ex.restype = ci
     lib.w4a16_dequant.argtypes = [p, sz, p, i64, i64, ci, u32, p]
     lib.w4a16_dequant.restype = ci
     lib.w4a16_mfma_layout_probe.argtypes = [p, p, p, u32, p]
@@ -213,6 +226,45 @@ def w4a16_gemm(X: torch.Tensor, packed: PackedW4, M: Optional[int] = None,
     _check(lib.w4a16_gemm(_ptr(X), _ptr(packed.data), packed.data.numel(), _ptr(Y), M, N, K, G,
                           flags, _ptr(workspace), 0 if workspace is None else workspace.numel(),
                           _stream(stream)), "w4a16_gemm")
+    return Y
+
+
+def w4a16_gemm_ex(X: torch.Tensor, packed: PackedW4, M: Optional[int] = None,
+                  Y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                  stream=None, *, col_scale: Optional[torch.Tensor] = None,
+                  bias: Optional[torch.Tensor] = None, aux: Optional[torch.Tensor] = None,
+                  activation: str = "none", aux_op: str = "add") -> torch.Tensor:
+    """w4a16_gemm with the fused output epilogue
+    Y = aux_op(act(X.deq * col_scale + bias), aux): col_scale fp32 [N], bias [N]
+    and aux [M][N] in X's dtype, each optional (device tensors)."""
+    lib = load_library()
+    if packed.layout_version != _layout_version:
+        raise W4A16Error(W4A16_ERR_INVALID_ARG, "w4a16_gemm_ex (blob layout version)")
+    K, N, G, flags = packed.K, packed.N, packed.group_size, packed.flags
+    if M is None:
+        M = X.shape[0]
+    if X.dtype != torch_dtype(flags) or X.numel() != M * K or not X.is_contiguous():
+        raise W4A16Error(W4A16_ERR_INVALID_ARG, "w4a16_gemm_ex (X dtype/shape)")
+    if col_scale is not None and (col_scale.dtype != torch.float32 or col_scale.numel() != N
+                                  or not col_scale.is_contiguous()):
+        raise W4A16Error(W4A16_ERR_INVALID_ARG, "w4a16_gemm_ex (col_scale)")
+    for name, t, n in (("bias", bias, N), ("aux", aux, M * N)):
+        if t is not None and (t.dtype != X.dtype or t.numel() != n or not t.is_contiguous()):
+            raise W4A16Error(W4A16_ERR_INVALID_ARG, f"w4a16_gemm_ex ({name})")
+    if activation not in W4A16_ACT or aux_op not in W4A16_AUX:
+        raise W4A16Error(W4A16_ERR_INVALID_ARG, "w4a16_gemm_ex (activation/aux_op)")
+    if Y is None:
+        Y = torch.empty((M, N), dtype=X.dtype, device=X.device)
+    if workspace is None:
+        workspace = workspace_for(_workspace_need(M, N, K, G, flags), X.device)
+    ep = Epilogue(None if col_scale is None else col_scale.data_ptr(),
+                  None if bias is None else bias.data_ptr(),
+                  None if aux is None else aux.data_ptr(), W4A16_ACT[activation],
+                  W4A16_AUX[aux_op])
+    _check(lib.w4a16_gemm_ex(_ptr(X), _ptr(packed.data), packed.data.numel(), _ptr(Y), M, N, K,
+                             G, flags, ctypes.byref(ep), _ptr(workspace),
+                             0 if workspace is None else workspace.numel(), _stream(stream)),
+           "w4a16_gemm_ex")
     return Y
 
 

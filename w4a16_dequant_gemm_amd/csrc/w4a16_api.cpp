@@ -151,6 +151,20 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int G, uint32_t /*flags*/) {
 
 }  // namespace w4a16
 
+namespace w4a16 {
+
+hipError_t launch_gemm(const void* X, const void* packed, void* Y, int64_t M, const Layout& L,
+                       bool bf16, const Plan& plan, void* workspace, const Epilogue& ep,
+                       hipStream_t stream) {
+    if (bf16)
+        return ep.any ? launch_gemm_bf16_ep(X, packed, Y, M, L, plan, workspace, ep, stream)
+                      : launch_gemm_bf16(X, packed, Y, M, L, plan, workspace, ep, stream);
+    return ep.any ? launch_gemm_f16_ep(X, packed, Y, M, L, plan, workspace, ep, stream)
+                  : launch_gemm_f16(X, packed, Y, M, L, plan, workspace, ep, stream);
+}
+
+}  // namespace w4a16
+
 using namespace w4a16;
 
 extern "C" {
@@ -214,9 +228,10 @@ size_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int group_size, ui
     return make_plan(M, N, K, group_size, flags).workspace;
 }
 
-w4a16_status_t w4a16_gemm(const void* X, const void* packed, size_t packed_bytes, void* Y,
-                          int64_t M, int64_t N, int64_t K, int group_size, uint32_t flags,
-                          void* workspace, size_t workspace_bytes, void* stream) {
+w4a16_status_t w4a16_gemm_ex(const void* X, const void* packed, size_t packed_bytes, void* Y,
+                             int64_t M, int64_t N, int64_t K, int group_size, uint32_t flags,
+                             const w4a16_epilogue_t* epilogue, void* workspace,
+                             size_t workspace_bytes, void* stream) {
     if (M < 1 || M >= kMaxDim) return W4A16_ERR_INVALID_ARG;
     w4a16_status_t st = check_shape(K, N, group_size, flags);
     if (st != W4A16_OK) return st;
@@ -225,6 +240,31 @@ w4a16_status_t w4a16_gemm(const void* X, const void* packed, size_t packed_bytes
     if ((double)M * (double)K >= (double)((int64_t)1 << 40) ||
         (double)M * (double)N >= (double)((int64_t)1 << 40))
         return W4A16_ERR_INVALID_ARG;
+    Epilogue ep;
+    memset(&ep, 0, sizeof(ep));
+    if (epilogue) {
+        const w4a16_epilogue_t& e = *epilogue;
+        if (e.activation < W4A16_ACT_NONE || e.activation > W4A16_ACT_SILU) return W4A16_ERR_INVALID_ARG;
+        if (e.aux_op != W4A16_AUX_ADD && e.aux_op != W4A16_AUX_MUL) return W4A16_ERR_INVALID_ARG;
+        if (((uintptr_t)e.col_scale & 3) || ((uintptr_t)e.bias & 1) || ((uintptr_t)e.aux & 1))
+            return W4A16_ERR_INVALID_ARG;
+        if (e.aux && e.aux != Y) {   // aux is Y itself (in place) or disjoint from it
+            const uintptr_t a0 = (uintptr_t)e.aux, y0 = (uintptr_t)Y;
+            const uintptr_t bytes = (uintptr_t)(M * N * 2);
+            if (a0 < y0 + bytes && y0 < a0 + bytes) return W4A16_ERR_INVALID_ARG;
+        }
+        // absent operands read harmless memory of at least their size: the
+        // blob (>= K*N/2 >= 16*N bytes) for [N] operands, Y for [M][N]
+        ep.has_scale = e.col_scale != nullptr;
+        ep.has_bias = e.bias != nullptr;
+        ep.has_aux = e.aux != nullptr;
+        ep.col_scale = e.col_scale ? e.col_scale : (const float*)packed;
+        ep.bias = (const uint16_t*)(e.bias ? e.bias : packed);
+        ep.aux = (const uint16_t*)(e.aux ? e.aux : Y);
+        ep.act = e.activation;
+        ep.aux_mul = e.aux_op == W4A16_AUX_MUL;
+        ep.any = ep.has_scale || ep.has_bias || ep.has_aux || e.activation != W4A16_ACT_NONE;
+    }
     const Layout L = make_layout(K, N, group_size, (flags & W4A16_SYM) != 0);
     if (packed_bytes < L.total) return W4A16_ERR_INVALID_ARG;
     const Plan plan = make_plan(M, N, K, group_size, flags);
@@ -233,7 +273,14 @@ w4a16_status_t w4a16_gemm(const void* X, const void* packed, size_t packed_bytes
             return W4A16_ERR_WORKSPACE;
     }
     return from_hip(launch_gemm(X, packed, Y, M, L, (flags & W4A16_BF16) != 0, plan, workspace,
-                                (hipStream_t)stream));
+                                ep, (hipStream_t)stream));
+}
+
+w4a16_status_t w4a16_gemm(const void* X, const void* packed, size_t packed_bytes, void* Y,
+                          int64_t M, int64_t N, int64_t K, int group_size, uint32_t flags,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    return w4a16_gemm_ex(X, packed, packed_bytes, Y, M, N, K, group_size, flags, nullptr,
+                         workspace, workspace_bytes, stream);
 }
 
 w4a16_status_t w4a16_dequant(const void* packed, size_t packed_bytes, void* W_out, int64_t K,

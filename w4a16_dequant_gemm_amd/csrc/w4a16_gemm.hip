@@ -40,6 +40,18 @@
 #include "w4a16_device.h"
 #include "w4a16_internal.h"
 
+// This file is compiled once per (activation dtype, epilogue) pair, each
+// object holding one quarter of the kernel instantiations (they compile in
+// parallel): W4A16_TU_BF16 selects bf16 over fp16, W4A16_TU_EP the kernels
+// with the output epilogue.  The (fp16, no epilogue) object also holds the
+// MFMA layout probe.
+#ifndef W4A16_TU_BF16
+#define W4A16_TU_BF16 0
+#endif
+#ifndef W4A16_TU_EP
+#define W4A16_TU_EP 0
+#endif
+
 namespace w4a16 {
 
 namespace {
@@ -85,6 +97,42 @@ __device__ __forceinline__ bool uses_exact_form(const uint8_t* packed, size_t t_
         const uint32_t flags = *(const uint32_t*)(packed + t_off + 8);
         return (flags & kFlagExactBf16) != 0;
     }
+}
+
+// ---------------------------------------------------------------------------
+// Output epilogue, run on the fp32 accumulator just before its one store.
+// Page "量化开销对比", sections 6.2, 6.6 and 6.7: after the k loop the result
+// is scaled per output channel, the bias added, and a residual or activation
+// applied inside the same kernel, so no further launch re-reads Y.  Each
+// step is optional; the order is t = v*c[n] + b[n], u = act(t), then
+// u + a[m][n] or u * a[m][n].  All in fp32, one rounding into the output dtype.
+// ---------------------------------------------------------------------------
+template <int DT>
+__device__ __forceinline__ float act_in(uint16_t b) {
+    if constexpr (DT == DT_F16)
+        return (float)__builtin_bit_cast(_Float16, b);
+    else
+        return __uint_as_float((uint32_t)b << 16);
+}
+
+// EP = false: the plain store.  EP = true: every pointer of ep is valid (the
+// host substitutes a harmless source for an absent operand), so each element
+// runs the same straight-line code: unconditional loads, then selects.
+template <int DT, bool EP>
+__device__ __forceinline__ uint16_t out_value(float v, int64_t row, int64_t col, int N,
+                                              const Epilogue& ep) {
+    if constexpr (EP) {
+        const float c = ep.has_scale ? ep.col_scale[col] : 1.0f;
+        const float b = ep.has_bias ? act_in<DT>(ep.bias[col]) : 0.0f;
+        const float a = act_in<DT>(ep.aux[row * N + col]);
+        const float t = v * c + b;
+        // SiLU as t * 1/(1 + 2^(-t*log2 e)) with the hardware exp2 and reciprocal
+        const float sg =
+            t * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-t * 1.4426950408889634f));
+        const float u = ep.act == kActSilu ? sg : (ep.act == kActRelu ? (t > 0.0f ? t : 0.0f) : t);
+        v = ep.has_aux ? (ep.aux_mul ? u * a : u + a) : u;
+    }
+    return round_out<DT>(v);
 }
 
 // ---------------------------------------------------------------------------
@@ -185,11 +233,11 @@ __device__ __forceinline__ WaveParts wave_parts(int s, int e, int nbat) {
 }
 
 // MB: 8, 16 or 32 >= M (sizes the LDS slots).
-template <int DT, bool SYM, int GS, int MB>
+template <int DT, bool SYM, int GS, int MB, bool EP>
 __global__ __launch_bounds__(SK_WAVES * 64) void splitk_kernel(
     const uint16_t* __restrict__ X, const uint8_t* __restrict__ packed, uint16_t* __restrict__ Y,
     float* __restrict__ part, uint32_t* __restrict__ cnt, int M, int N, int K, int nbat, int base,
-    int rem, size_t s_off, size_t z_off, size_t t_off) {
+    int rem, size_t s_off, size_t z_off, size_t t_off, Epilogue ep) {
     constexpr int SPG = GS < SK_U ? GS : SK_U;   // k-steps per group inside a batch
     constexpr int NGB = SK_U / SPG;              // groups (or group parts) per batch
     constexpr int QMAX = MB / 8;                 // 8-row accumulator groups that can hold rows < M
@@ -295,7 +343,8 @@ __global__ __launch_bounds__(SK_WAVES * 64) void splitk_kernel(
 
     // Accumulators of a whole column block straight to Y.
     auto to_y = [&](int nb) {
-        uint16_t* ybase = Y + (size_t)(4 * (lane >> 5)) * N + (size_t)nb * kColBlock + (lane & 31);
+        const int64_t col0 = (int64_t)nb * kColBlock + (lane & 31);
+        uint16_t* ybase = Y + (size_t)(4 * (lane >> 5)) * N + col0;
 #pragma unroll
         for (int q = 0; q < QMAX; ++q) {
             if (q >= QM) break;
@@ -304,7 +353,9 @@ __global__ __launch_bounds__(SK_WAVES * 64) void splitk_kernel(
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int row = 8 * q + 4 * (lane >> 5) + i;
-                    if (row < M) ybase[(size_t)(8 * q + i) * N + 32 * t] = round_out<DT>(acc[t][4 * q + i]);
+                    if (row < M)
+                        ybase[(size_t)(8 * q + i) * N + 32 * t] =
+                            out_value<DT, EP>(acc[t][4 * q + i], row, col0 + 32 * t, N, ep);
                 }
         }
     };
@@ -428,7 +479,8 @@ __global__ __launch_bounds__(SK_WAVES * 64) void splitk_kernel(
                     const int row = 8 * q + row0 + j;
                     if (row >= M) continue;
                     if (inside)
-                        Y[(size_t)row * N + col0 + 32 * t] = round_out<DT>(v[j]);
+                        Y[(size_t)row * N + col0 + 32 * t] =
+                            out_value<DT, EP>(v[j], row, (int64_t)col0 + 32 * t, N, ep);
                     else
                         st_dev(&my_slot[(t * M + row) * 32 + (lane & 31)], v[j]);
                 }
@@ -446,7 +498,8 @@ __global__ __launch_bounds__(SK_WAVES * 64) void splitk_kernel(
                 const int f = (t * M + row) * 32 + (tid & 31);
                 float sum = ld_dev(&slot_of(g0)[f]);
                 for (int g = g0 + 1; g <= g1; ++g) sum += ld_dev(&slot_of(g)[f]);
-                Y[(size_t)row * N + (size_t)nb * kColBlock + 32 * t + (tid & 31)] = round_out<DT>(sum);
+                const int64_t col = (int64_t)nb * kColBlock + 32 * t + (tid & 31);
+                Y[(size_t)row * N + col] = out_value<DT, EP>(sum, row, col, N, ep);
             }
         if (tid == 0) reset_counter(&cnt[g0]);
     }
@@ -471,11 +524,12 @@ __global__ __launch_bounds__(SK_WAVES * 64) void splitk_kernel(
 // ---------------------------------------------------------------------------
 constexpr int TK_WAVES = 8;
 
-template <int DT, bool SYM, int GS, int MT, bool FULL>
+template <int DT, bool SYM, int GS, int MT, bool FULL, bool EP>
 __global__ __launch_bounds__(TK_WAVES * 64) void tiled_kernel(
     const uint16_t* __restrict__ X, const uint8_t* __restrict__ packed, uint16_t* __restrict__ Y,
     float* __restrict__ part, uint32_t* __restrict__ cnt, int M, int N, int K,
-    int steps_per_split, int S, size_t s_off, size_t z_off, size_t t_off) {
+    int steps_per_split, int S, size_t s_off, size_t z_off, size_t t_off,
+    Epilogue ep) {
     constexpr int KT = kTiledStage;             // k-steps per stage
     constexpr int ROWS = 32 * MT;
     constexpr int CPR = 2 * KT;                 // 16-byte chunks per row and stage
@@ -752,7 +806,9 @@ __global__ __launch_bounds__(TK_WAVES * 64) void tiled_kernel(
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
                         const int rr = m0 + 32 * r + acc_row(i, lane);
-                        if (rr < M) Y[(int64_t)rr * N + colw + 32 * tt] = round_out<DT>(acc[r][tt][i]);
+                        if (rr < M)
+                            Y[(int64_t)rr * N + colw + 32 * tt] =
+                                out_value<DT, EP>(acc[r][tt][i], rr, (int64_t)colw + 32 * tt, N, ep);
                     }
         }
         return;
@@ -817,7 +873,9 @@ __global__ __launch_bounds__(TK_WAVES * 64) void tiled_kernel(
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int rr = m0 + 32 * r + acc_row(4 * j + e, lane);
-                    if (rr < M) Y[(int64_t)rr * N + colw + 32 * tt] = round_out<DT>(v[g][e]);
+                    if (rr < M)
+                        Y[(int64_t)rr * N + colw + 32 * tt] =
+                            out_value<DT, EP>(v[g][e], rr, (int64_t)colw + 32 * tt, N, ep);
                 }
             }
         }
@@ -827,6 +885,7 @@ __global__ __launch_bounds__(TK_WAVES * 64) void tiled_kernel(
 // ---------------------------------------------------------------------------
 // One MFMA with the kernels' operand and accumulator placement.
 // ---------------------------------------------------------------------------
+#if !W4A16_TU_BF16 && !W4A16_TU_EP
 template <int DT>
 __global__ __launch_bounds__(64) void mfma_probe_kernel(const uint16_t* __restrict__ A,
                                                         const uint16_t* __restrict__ B,
@@ -846,83 +905,104 @@ __global__ __launch_bounds__(64) void mfma_probe_kernel(const uint16_t* __restri
 #pragma unroll
     for (int r = 0; r < 16; ++r) D[acc_row(r, lane) * 32 + (lane & 31)] = c[r];
 }
+#endif
 
 template <int DT, bool SYM, int GS, int MB>
 void launch_splitk_mb(const void* X, const void* packed, void* Y, int64_t M, const Layout& L,
-                      const Plan& p, float* part, uint32_t* cnt, hipStream_t stream) {
-    hipLaunchKernelGGL((splitk_kernel<DT, SYM, GS, MB>), dim3(p.grid_x), dim3(SK_WAVES * 64), 0,
-                       stream, (const uint16_t*)X, (const uint8_t*)packed, (uint16_t*)Y, part, cnt,
-                       (int)M, (int)L.N, (int)L.K, p.nbat, p.base, p.rem, L.s_off, L.z_off,
-                       L.t_off);
+                      const Plan& p, float* part, uint32_t* cnt, hipStream_t stream,
+                   const Epilogue& ep) {
+    hipLaunchKernelGGL((splitk_kernel<DT, SYM, GS, MB, W4A16_TU_EP != 0>), dim3(p.grid_x),
+                       dim3(SK_WAVES * 64), 0, stream, (const uint16_t*)X, (const uint8_t*)packed,
+                       (uint16_t*)Y, part, cnt, (int)M, (int)L.N, (int)L.K, p.nbat, p.base,
+                       p.rem, L.s_off, L.z_off, L.t_off, ep);
 }
 
 template <int DT, bool SYM, int GS>
 void launch_splitk(const void* X, const void* packed, void* Y, int64_t M, const Layout& L,
-                   const Plan& p, float* part, uint32_t* cnt, hipStream_t stream) {
-    if (M <= 8) launch_splitk_mb<DT, SYM, GS, 8>(X, packed, Y, M, L, p, part, cnt, stream);
-    else if (M <= 16) launch_splitk_mb<DT, SYM, GS, 16>(X, packed, Y, M, L, p, part, cnt, stream);
-    else launch_splitk_mb<DT, SYM, GS, 32>(X, packed, Y, M, L, p, part, cnt, stream);
+                   const Plan& p, float* part, uint32_t* cnt, hipStream_t stream,
+                   const Epilogue& ep) {
+    if (M <= 8) launch_splitk_mb<DT, SYM, GS, 8>(X, packed, Y, M, L, p, part, cnt, stream, ep);
+    else if (M <= 16) launch_splitk_mb<DT, SYM, GS, 16>(X, packed, Y, M, L, p, part, cnt, stream, ep);
+    else launch_splitk_mb<DT, SYM, GS, 32>(X, packed, Y, M, L, p, part, cnt, stream, ep);
 }
 
 template <int DT, bool SYM, int GS, int MT, bool FULL>
 void launch_tiled_mt(const void* X, const void* packed, void* Y, int64_t M, const Layout& L,
-                     const Plan& p, float* part, uint32_t* cnt, hipStream_t stream) {
-    hipLaunchKernelGGL((tiled_kernel<DT, SYM, GS, MT, FULL>), dim3(p.grid_x, p.grid_y, p.grid_z),
-                       dim3(TK_WAVES * 64), 0, stream, (const uint16_t*)X, (const uint8_t*)packed,
-                       (uint16_t*)Y, part, cnt, (int)M, (int)L.N, (int)L.K, p.steps_per_split,
-                       p.splits, L.s_off, L.z_off, L.t_off);
+                     const Plan& p, float* part, uint32_t* cnt, hipStream_t stream,
+                   const Epilogue& ep) {
+    hipLaunchKernelGGL((tiled_kernel<DT, SYM, GS, MT, FULL, W4A16_TU_EP != 0>),
+                       dim3(p.grid_x, p.grid_y, p.grid_z), dim3(TK_WAVES * 64), 0, stream,
+                       (const uint16_t*)X, (const uint8_t*)packed, (uint16_t*)Y, part, cnt, (int)M,
+                       (int)L.N, (int)L.K, p.steps_per_split, p.splits, L.s_off, L.z_off, L.t_off,
+                       ep);
 }
 
 // FULL: every stage of every split has all its k-steps (K a multiple of the
 // stage depth, 128), which the interleaved schedule assumes.
 template <int DT, bool SYM, int GS>
 void launch_tiled(const void* X, const void* packed, void* Y, int64_t M, const Layout& L,
-                  const Plan& p, float* part, uint32_t* cnt, hipStream_t stream) {
+                  const Plan& p, float* part, uint32_t* cnt, hipStream_t stream,
+                   const Epilogue& ep) {
     const bool full = (L.K / kKStep) % kTiledStage == 0;
     if (p.mt == 2) {
-        if (full) launch_tiled_mt<DT, SYM, GS, 2, true>(X, packed, Y, M, L, p, part, cnt, stream);
-        else launch_tiled_mt<DT, SYM, GS, 2, false>(X, packed, Y, M, L, p, part, cnt, stream);
+        if (full) launch_tiled_mt<DT, SYM, GS, 2, true>(X, packed, Y, M, L, p, part, cnt, stream, ep);
+        else launch_tiled_mt<DT, SYM, GS, 2, false>(X, packed, Y, M, L, p, part, cnt, stream, ep);
     } else {
-        if (full) launch_tiled_mt<DT, SYM, GS, 4, true>(X, packed, Y, M, L, p, part, cnt, stream);
-        else launch_tiled_mt<DT, SYM, GS, 4, false>(X, packed, Y, M, L, p, part, cnt, stream);
+        if (full) launch_tiled_mt<DT, SYM, GS, 4, true>(X, packed, Y, M, L, p, part, cnt, stream, ep);
+        else launch_tiled_mt<DT, SYM, GS, 4, false>(X, packed, Y, M, L, p, part, cnt, stream, ep);
     }
 }
 
 template <int DT, bool SYM>
 void launch_variant(const void* X, const void* packed, void* Y, int64_t M, const Layout& L,
-                    const Plan& p, float* part, uint32_t* cnt, hipStream_t stream) {
+                    const Plan& p, float* part, uint32_t* cnt, hipStream_t stream,
+                   const Epilogue& ep) {
     const int GS = (int)(L.G / kKStep);
     if (p.variant == VARIANT_SPLITK) {
-        if (GS == 8) launch_splitk<DT, SYM, 8>(X, packed, Y, M, L, p, part, cnt, stream);
-        else if (GS == 4) launch_splitk<DT, SYM, 4>(X, packed, Y, M, L, p, part, cnt, stream);
-        else launch_splitk<DT, SYM, 2>(X, packed, Y, M, L, p, part, cnt, stream);
+        if (GS == 8) launch_splitk<DT, SYM, 8>(X, packed, Y, M, L, p, part, cnt, stream, ep);
+        else if (GS == 4) launch_splitk<DT, SYM, 4>(X, packed, Y, M, L, p, part, cnt, stream, ep);
+        else launch_splitk<DT, SYM, 2>(X, packed, Y, M, L, p, part, cnt, stream, ep);
     } else {
-        if (GS == 8) launch_tiled<DT, SYM, 8>(X, packed, Y, M, L, p, part, cnt, stream);
-        else if (GS == 4) launch_tiled<DT, SYM, 4>(X, packed, Y, M, L, p, part, cnt, stream);
-        else launch_tiled<DT, SYM, 2>(X, packed, Y, M, L, p, part, cnt, stream);
+        if (GS == 8) launch_tiled<DT, SYM, 8>(X, packed, Y, M, L, p, part, cnt, stream, ep);
+        else if (GS == 4) launch_tiled<DT, SYM, 4>(X, packed, Y, M, L, p, part, cnt, stream, ep);
+        else launch_tiled<DT, SYM, 2>(X, packed, Y, M, L, p, part, cnt, stream, ep);
     }
 }
 
 }  // namespace
 
-hipError_t launch_gemm(const void* X, const void* packed, void* Y, int64_t M, const Layout& L,
-                       bool bf16, const Plan& p, void* workspace, hipStream_t stream) {
+// This object's share of launch_gemm: one activation dtype, with or without
+// the epilogue.
+#if W4A16_TU_BF16
+#if W4A16_TU_EP
+#define W4A16_TU_ENTRY launch_gemm_bf16_ep
+#else
+#define W4A16_TU_ENTRY launch_gemm_bf16
+#endif
+#else
+#if W4A16_TU_EP
+#define W4A16_TU_ENTRY launch_gemm_f16_ep
+#else
+#define W4A16_TU_ENTRY launch_gemm_f16
+#endif
+#endif
+
+hipError_t W4A16_TU_ENTRY(const void* X, const void* packed, void* Y, int64_t M, const Layout& L,
+                          const Plan& p, void* workspace, const Epilogue& ep,
+                          hipStream_t stream) {
+    constexpr int DT = W4A16_TU_BF16 ? DT_BF16 : DT_F16;
     uint32_t* cnt = nullptr;
     float* part = nullptr;
     if (p.splits > 1) {
         cnt = (uint32_t*)workspace;
         part = (float*)((uint8_t*)workspace + p.counters_bytes);
     }
-    if (bf16) {
-        if (L.sym) launch_variant<DT_BF16, true>(X, packed, Y, M, L, p, part, cnt, stream);
-        else launch_variant<DT_BF16, false>(X, packed, Y, M, L, p, part, cnt, stream);
-    } else {
-        if (L.sym) launch_variant<DT_F16, true>(X, packed, Y, M, L, p, part, cnt, stream);
-        else launch_variant<DT_F16, false>(X, packed, Y, M, L, p, part, cnt, stream);
-    }
+    if (L.sym) launch_variant<DT, true>(X, packed, Y, M, L, p, part, cnt, stream, ep);
+    else launch_variant<DT, false>(X, packed, Y, M, L, p, part, cnt, stream, ep);
     return hipGetLastError();
 }
 
+#if !W4A16_TU_BF16 && !W4A16_TU_EP
 hipError_t launch_mfma_probe(const void* A, const void* B, float* D, bool bf16,
                              hipStream_t stream) {
     if (bf16)
@@ -933,5 +1013,6 @@ hipError_t launch_mfma_probe(const void* A, const void* B, float* D, bool bf16,
                            (const uint16_t*)A, (const uint16_t*)B, D);
     return hipGetLastError();
 }
+#endif
 
 }  // namespace w4a16

@@ -35,6 +35,22 @@ struct Plan {
 
 Plan make_plan(int64_t M, int64_t N, int64_t K, int G, uint32_t flags);
 
+// Output epilogue of one call.  When any step is active every pointer is
+// valid device memory: an absent column scale or bias points at the blob and
+// an absent aux at Y (read, never used), so the kernels load unconditionally.
+constexpr int kActNone = 0;
+constexpr int kActRelu = 1;
+constexpr int kActSilu = 2;
+struct Epilogue {
+    const float* col_scale;   // [N]
+    const uint16_t* bias;     // [N] in the activation dtype
+    const uint16_t* aux;      // [M][N] in the activation dtype
+    int has_scale, has_bias, has_aux;
+    int act;                  // kAct*
+    int aux_mul;              // 0: y = u + aux, 1: y = u * aux
+    int any;                  // nonzero when some step is active
+};
+
 // Launchers return the hipError_t of the launch (hipGetLastError()).
 hipError_t launch_repack(const uint32_t* qweight, const void* scales, const uint8_t* zeros,
                          const Layout& L, bool bf16, void* packed, hipStream_t stream);
@@ -43,7 +59,17 @@ hipError_t launch_unrepack(const void* packed, const Layout& L, bool bf16, uint3
 hipError_t launch_dequant(const void* packed, const Layout& L, bool bf16, void* W_out,
                           hipStream_t stream);
 hipError_t launch_gemm(const void* X, const void* packed, void* Y, int64_t M, const Layout& L,
-                       bool bf16, const Plan& plan, void* workspace, hipStream_t stream);
+                       bool bf16, const Plan& plan, void* workspace, const Epilogue& ep,
+                       hipStream_t stream);
+// The four objects of w4a16_gemm.hip, one per (dtype, epilogue) pair.
+#define W4A16_DECLARE_GEMM_PART(name)                                                        \
+    hipError_t name(const void* X, const void* packed, void* Y, int64_t M, const Layout& L, \
+                    const Plan& plan, void* workspace, const Epilogue& ep, hipStream_t stream);
+W4A16_DECLARE_GEMM_PART(launch_gemm_f16)
+W4A16_DECLARE_GEMM_PART(launch_gemm_f16_ep)
+W4A16_DECLARE_GEMM_PART(launch_gemm_bf16)
+W4A16_DECLARE_GEMM_PART(launch_gemm_bf16_ep)
+#undef W4A16_DECLARE_GEMM_PART
 hipError_t launch_mfma_probe(const void* A, const void* B, float* D, bool bf16,
                              hipStream_t stream);
 
