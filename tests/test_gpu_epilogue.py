@@ -125,3 +125,41 @@ def test_epilogue_rejects_bad_arguments():
                             d.packed.data.numel(), ctypes.c_void_p(Yv.data_ptr()), 2, 128, 256, 128,
                             d.flags, ctypes.byref(ep), None, 0, None)
     assert st == w4.W4A16_ERR_INVALID_ARG
+
+
+# Full-size shapes of a decoder FFN block, as the fused-block benchmark runs them:
+# (workload, epilogue) with sampled outputs against the oracle.
+FULL = [
+    ("decode_m1_k8192_n28672_fp16_asym_g128_outliers", "silu", None),
+    ("decode_m8_k8192_n28672_fp16_asym_g128_outliers", "none", "mul"),
+    ("transition_m16_k28672_n8192_bf16_sym_g128", "none", "add"),
+    ("batch_m64_k8192_n28672_fp16_asym_g64", "silu", "add"),
+]
+
+
+@pytest.mark.parametrize("name,act,aux_op", FULL, ids=[f[0] for f in FULL])
+def test_full_size_epilogue(name, act, aux_op):
+    w4 = lib()
+    p = synth.workload(name)
+    say(f"full-size epilogue {name}: act={act} aux={aux_op}")
+    d = OnDevice(p)
+    cs, bias, aux = operands(p, seed=3)
+    tdt = w4.torch_dtype(d.flags)
+    dev = d.X.device
+    cs_t = torch.from_numpy(cs).to(dev)
+    bias_t = torch.from_numpy(bias.view(np.int16)).view(tdt).to(dev)
+    aux_t = torch.from_numpy(aux.view(np.int16)).view(tdt).to(dev) if aux_op else None
+    Y = w4.w4a16_gemm_ex(d.X, d.packed, col_scale=cs_t, bias=bias_t, aux=aux_t,
+                         activation=act, aux_op=aux_op or "add")
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(2)
+    ms = np.concatenate([rng.integers(0, p.M, 256), np.full(16, p.M - 1)])
+    ns = np.concatenate([rng.integers(0, p.N, 256), np.arange(16) + p.N - 16])
+    Yref, B = oracle.gemm_at(p.X, p.qweight, p.scales, p.zeros, p.M, p.N, p.K, p.G, p.dtype,
+                             p.sym, ms, ns)
+    Yo, Bo = oracle.epilogue(Yref, B, p.M, p.N, p.dtype, col_scale=cs, bias=bias,
+                             aux=aux if aux_op else None, activation=act,
+                             aux_op=aux_op or "add", ms=ms, ns=ns)
+    Yg = d.y_float(Y)[ms, ns]
+    rel, zero_ok = oracle.max_rel_error(Yg, Yo, Bo)
+    assert zero_ok and rel <= TOL[p.dtype], f"{name}: max|Y-Yref|/Bo = {rel:.3e}"
