@@ -163,3 +163,25 @@ def test_full_size_epilogue(name, act, aux_op):
     Yg = d.y_float(Y)[ms, ns]
     rel, zero_ok = oracle.max_rel_error(Yg, Yo, Bo)
     assert zero_ok and rel <= TOL[p.dtype], f"{name}: max|Y-Yref|/Bo = {rel:.3e}"
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("path", PATHS, ids=[q[0] for q in PATHS])
+def test_neutral_epilogue_is_bitwise_the_plain_product(path, dtype):
+    """Column scale 1 and bias 0 run the epilogue kernels through every step
+    (t = v*1 + 0, identity) and must store exactly what the plain kernels
+    store (up to the sign of zero)."""
+    from gpu_helpers import same_bits
+    _, M, K, N, G, variant, extra = path
+    sym = dtype == "bf16"
+    p = synth.make_problem(M, K, N, G=G, dtype=dtype, sym=sym, seed=7 * M + N)
+    d = OnDevice(p)
+    w4 = d.w4
+    ones = torch.ones(N, dtype=torch.float32, device=d.X.device)
+    zeros = torch.zeros(N, dtype=w4.torch_dtype(d.flags), device=d.X.device)
+    say(f"neutral epilogue {path[0]} / {dtype}")
+    with env(W4A16_FORCE_VARIANT=variant, **extra):
+        Y0 = w4.w4a16_gemm(d.X, d.packed)
+        Y1 = w4.w4a16_gemm_ex(d.X, d.packed, col_scale=ones, bias=zeros)
+    torch.cuda.synchronize()
+    assert same_bits(w4.bits_of(Y0), w4.bits_of(Y1))
