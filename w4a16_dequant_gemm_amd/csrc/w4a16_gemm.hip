@@ -434,12 +434,25 @@ __global__ __launch_bounds__(SK_WAVES * 64) void splitk_kernel(
     // Elements of a partial tile: (t, q) pairs of f32x4 per lane, pair t*QM + q
     // handled by wave (t*QM + q) % SK_WAVES.
     auto mine = [&](int t, int q) { return q < QM && ((t * QM + q) % SK_WAVES) == wave; };
-    int done = -1;
-    for (int p = 0; p < 2 * SK_WAVES; ++p) {
-        const WaveParts pw = s_parts[p >> 1];
-        const int nb = (p & 1) ? pw.tail : pw.head;
-        if (nb < 0 || nb == done) continue;
-        done = nb;
+    // The waves' partial blocks, read once into (wave-uniform) registers;
+    // blocks are visited in increasing order, each once.
+    int heads[SK_WAVES], tails[SK_WAVES];
+#pragma unroll
+    for (int w = 0; w < SK_WAVES; ++w) {
+        const WaveParts pw = s_parts[w];
+        heads[w] = __builtin_amdgcn_readfirstlane(pw.head);
+        tails[w] = __builtin_amdgcn_readfirstlane(pw.tail);
+    }
+    auto next_part = [&](int after) {   // smallest partial block > after, or -1
+        int n = 0x7fffffff;
+#pragma unroll
+        for (int w = 0; w < SK_WAVES; ++w) {
+            if (heads[w] > after) n = min(n, heads[w]);
+            if (tails[w] > after) n = min(n, tails[w]);
+        }
+        return n == 0x7fffffff ? -1 : n;
+    };
+    for (int nb = next_part(-1); nb >= 0; nb = next_part(nb)) {
         __syncthreads();   // the previous block's slots have been read
         if (my_tail == nb) to_slot();
         __syncthreads();
@@ -468,8 +481,7 @@ __global__ __launch_bounds__(SK_WAVES * 64) void splitk_kernel(
                 bool first = true;
 #pragma unroll
                 for (int w = 0; w < SK_WAVES; ++w) {
-                    const WaveParts ow = s_parts[w];
-                    if (ow.head != nb && ow.tail != nb) continue;
+                    if (heads[w] != nb && tails[w] != nb) continue;
                     const f32x4 sv = slots[w][t][q][lane];
                     v = first ? sv : v + sv;
                     first = false;
