@@ -77,7 +77,21 @@ def cpu_baseline(name, cfg, budget_s=12.0):
     import oracle
 
     oracle.build()
-    threads = os.cpu_count() or 1
+    # this process's CPU share (at most 16 threads, one GPU's share of its host)
+    try:
+        threads = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        threads = os.cpu_count() or 1
+    threads = max(1, min(threads, 16))
+    cpu_model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     p = synth.workload(name)
     M, K, N, G = cfg["M"], cfg["K"], cfg["N"], cfg["G"]
     rows = min(M, 64)
@@ -106,7 +120,7 @@ def cpu_baseline(name, cfg, budget_s=12.0):
         "cores": threads,
         "kind": "oracle",
         "sample": f"{rows} of {M} rows x {ncol} of {N} columns (K={K}) of the same workload, "
-                  f"{len(times)} runs, {t:.2f} s each on {threads} threads (the C oracle: "
+                  f"{len(times)} runs, {t:.2f} s each on {threads} threads of {cpu_model} (the C oracle: "
                   f"per-element dequant with its own RNE, fp64 dot products); rate "
                   f"extrapolated linearly to the full {M}x{N} output ({t_full:.2f} s)",
     }
