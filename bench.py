@@ -219,6 +219,33 @@ def run_workload(name, steps, warmup, rotate_bytes=1 << 30, with_cpu=True, compa
     per_launch = np.array([a.elapsed_time(b) for a, b in ev])
     kern_ms = float(np.mean(per_launch))
 
+    # Practical read ceiling on the same bytes: the weight blobs read with the
+    # split-K kernel's load pattern and no compute (w4a16_read_probe), timed the
+    # same way (one graph of 50 calls over the rotating copies).
+    read_gbs = None
+    try:
+        pbytes = base.data.numel() // 1024 * 1024
+        pout = torch.empty(w4.w4a16_read_probe_out_bytes(), dtype=torch.uint8, device=dev)
+        for i in range(5):
+            w4.w4a16_read_probe(blobs[i % copies].data, pbytes, out=pout)
+        torch.cuda.synchronize()
+        pg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(pg):
+            for i in range(50):
+                w4.w4a16_read_probe(blobs[i % copies].data, pbytes, out=pout)
+        torch.cuda.synchronize()
+        pg.replay()
+        torch.cuda.synchronize()
+        t0.record(stream)
+        pg.replay()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        read_gbs = pbytes / (t0.elapsed_time(t1) / 50 * 1e-3) / 1e9
+        del pg, pout
+    except RuntimeError as e:
+        read_gbs = None
+        print(f"read probe skipped: {str(e)[:120]}", file=sys.stderr)
+
     nbytes = algorithmic_bytes(cfg)
     flops = algorithmic_flops(cfg)
     bound = bound_of(cfg)
@@ -259,6 +286,9 @@ def run_workload(name, steps, warmup, rotate_bytes=1 << 30, with_cpu=True, compa
         "algorithmic_bytes": nbytes,
         "kernel_source_hash": kernel_source_hash(),
         "weight_only_gbs": round((p.K * p.N // 2) / (ms_step * 1e-3) / 1e9, 1),
+        "read_probe_gbs": None if read_gbs is None else round(read_gbs, 1),
+        "frac_of_read_probe": None if read_gbs is None else round(
+            nbytes / (ms_step * 1e-3) / 1e9 / read_gbs, 4),
         "roofline": roof,
     }
     if comparators:

@@ -197,6 +197,21 @@ w4a16_status_t w4a16_dequant(const void *packed, size_t packed_bytes, void *W_ou
                              void *stream);
 
 /*
+ * Measurement aid: the practical read ceiling of the weight stream.  Reads
+ * `bytes` (a multiple of 1024, buf 16-byte aligned, device memory) once with
+ * the split-K kernel's load pattern (balanced contiguous ranges of 1 KiB
+ * chunks over 256 workgroups of 8 waves, 16-byte non-temporal loads, two
+ * batches of two in flight per wave) and no arithmetic besides an XOR; each
+ * of the w4a16_read_probe_out_bytes() / 16 threads writes its XOR (16 bytes)
+ * to out, so the XOR of out is the XOR of the buffer.  The GEMM's HBM rate
+ * is reported against this ceiling as well as against the 8 TB/s figure.
+ * Errors: INVALID_ARG (pointers, alignment, size), HIP.
+ */
+size_t w4a16_read_probe_out_bytes(void);
+w4a16_status_t w4a16_read_probe(const void *buf, size_t bytes, void *out, size_t out_bytes,
+                                void *stream);
+
+/*
  * Diagnostic: one v_mfma_f32_32x32x16 (fp16 or bf16 per flags) on A[32][16]
  * and B[16][32] (row-major, dev), loaded into the operand registers the way
  * the GEMM kernels load them, with D[32][32] (fp32, row-major, dev) written

@@ -150,6 +150,13 @@ def test_dequant_and_probe_reject(lib):
     assert lib.w4a16_dequant(FAKE, 1 << 30, FAKE, 256, 200, 128, 0, None) == w4.W4A16_ERR_UNSUPPORTED
     assert lib.w4a16_mfma_layout_probe(FAKE, FAKE, NULL, 0, None) == w4.W4A16_ERR_INVALID_ARG
     assert lib.w4a16_mfma_layout_probe(FAKE, FAKE, FAKE, 0x2, None) == w4.W4A16_ERR_INVALID_ARG
+    ob = lib.w4a16_read_probe_out_bytes()
+    assert ob == 256 * 512 * 16
+    assert lib.w4a16_read_probe(FAKE, 1000, FAKE, ob, None) == w4.W4A16_ERR_INVALID_ARG     # not 1 KiB
+    assert lib.w4a16_read_probe(FAKE, 0, FAKE, ob, None) == w4.W4A16_ERR_INVALID_ARG
+    assert lib.w4a16_read_probe(FAKE, 4096, FAKE, ob - 16, None) == w4.W4A16_ERR_INVALID_ARG
+    assert lib.w4a16_read_probe(FAKE_MIS, 4096, FAKE, ob, None) == w4.W4A16_ERR_INVALID_ARG
+    assert lib.w4a16_read_probe(NULL, 4096, FAKE, ob, None) == w4.W4A16_ERR_INVALID_ARG
 
 
 def test_python_binding_fails_loudly_without_library(tmp_path):

@@ -292,3 +292,19 @@ def test_full_size_workload(name):
     sl = column_slice(p, cols)
     want = oracle.dequant(sl.qweight, sl.scales, sl.zeros, p.K, 128, p.G, p.dtype, p.sym)
     assert same_bits(got, want)
+
+
+@pytest.mark.parametrize("nbytes", [1024, 3 * (1 << 20) + 5 * 1024, 117440512])
+def test_read_probe_reads_every_byte_once(nbytes):
+    """The read-bandwidth probe behind the benchmark's ceiling: XOR of its
+    per-thread outputs equals the XOR of the buffer's 16-byte words."""
+    w4 = lib()
+    rng = np.random.default_rng(nbytes % 1000)
+    host = rng.integers(0, 2**32, size=nbytes // 4, dtype=np.uint32)
+    buf = torch.from_numpy(host.view(np.int32)).cuda()
+    say(f"read probe over {nbytes} bytes")
+    out = w4.w4a16_read_probe(buf, nbytes)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32).reshape(-1, 4), axis=0)
+    want = np.bitwise_xor.reduce(host.reshape(-1, 4), axis=0)
+    assert np.array_equal(got, want)

@@ -34,7 +34,7 @@ W4A16_SYM = 0x2
 C_FUNCTIONS = (
     "w4a16_abi_version", "w4a16_layout_version", "w4a16_status_string", "w4a16_packed_bytes",
     "w4a16_repack", "w4a16_unrepack", "w4a16_workspace_bytes", "w4a16_gemm", "w4a16_dequant",
-    "w4a16_mfma_layout_probe", "w4a16_gemm_ex",
+    "w4a16_mfma_layout_probe", "w4a16_gemm_ex", "w4a16_read_probe", "w4a16_read_probe_out_bytes",
 )
 
 
@@ -91,6 +91,9 @@ def load_library(path: str = LIB_PATH):
     lib.w4a16_dequant.restype = ci
     lib.w4a16_mfma_layout_probe.argtypes = [p, p, p, u32, p]
     lib.w4a16_mfma_layout_probe.restype = ci
+    lib.w4a16_read_probe_out_bytes.restype = sz
+    lib.w4a16_read_probe.argtypes = [p, sz, p, sz, p]
+    lib.w4a16_read_probe.restype = ci
     global _layout_version
     _layout_version = lib.w4a16_layout_version()
     _ws_bytes.clear()
@@ -277,6 +280,25 @@ def w4a16_dequant(packed: PackedW4, W_out: Optional[torch.Tensor] = None,
                                         N, packed.group_size, packed.flags, _stream(stream)),
            "w4a16_dequant")
     return W_out
+
+
+def w4a16_read_probe_out_bytes() -> int:
+    return int(load_library().w4a16_read_probe_out_bytes())
+
+
+def w4a16_read_probe(buf: torch.Tensor, nbytes: Optional[int] = None,
+                     out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Read nbytes (default: all of buf, rounded down to 1 KiB) of a device
+    buffer with the decode kernel's load pattern; returns the per-thread XORs
+    (uint8 tensor of w4a16_read_probe_out_bytes() bytes)."""
+    lib = load_library()
+    if nbytes is None:
+        nbytes = (buf.numel() * buf.element_size()) // 1024 * 1024
+    if out is None:
+        out = torch.empty(w4a16_read_probe_out_bytes(), dtype=torch.uint8, device=buf.device)
+    _check(lib.w4a16_read_probe(_ptr(buf), nbytes, _ptr(out), out.numel(), _stream(stream)),
+           "w4a16_read_probe")
+    return out
 
 
 def w4a16_mfma_layout_probe(A: torch.Tensor, B: torch.Tensor, flags: int,

@@ -294,6 +294,16 @@ w4a16_status_t w4a16_dequant(const void* packed, size_t packed_bytes, void* W_ou
                                    (hipStream_t)stream));
 }
 
+size_t w4a16_read_probe_out_bytes(void) { return (size_t)kProbeBlocks * kProbeThreads * 16; }
+
+w4a16_status_t w4a16_read_probe(const void* buf, size_t bytes, void* out, size_t out_bytes,
+                                void* stream) {
+    if (!buf || !out || !aligned16(buf) || !aligned16(out)) return W4A16_ERR_INVALID_ARG;
+    if (bytes == 0 || bytes % kChunkBytes != 0) return W4A16_ERR_INVALID_ARG;
+    if (out_bytes < w4a16_read_probe_out_bytes()) return W4A16_ERR_INVALID_ARG;
+    return from_hip(launch_read_probe(buf, bytes, out, (hipStream_t)stream));
+}
+
 w4a16_status_t w4a16_mfma_layout_probe(const void* A, const void* B, float* D, uint32_t flags,
                                        void* stream) {
     if (flags & ~W4A16_BF16) return W4A16_ERR_INVALID_ARG;

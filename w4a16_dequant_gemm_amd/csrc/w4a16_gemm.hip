@@ -1015,6 +1015,54 @@ hipError_t W4A16_TU_ENTRY(const void* X, const void* packed, void* Y, int64_t M,
 }
 
 #if !W4A16_TU_BF16 && !W4A16_TU_EP
+// Read-bandwidth probe: the decode kernel's load pattern with no compute.
+// The buffer is nchunk 1 KiB chunks, dealt out in balanced contiguous ranges
+// to the grid's waves; each lane issues one 16-byte non-temporal load per
+// chunk, two batches of two chunks in flight, and XORs what it read (each
+// chunk exactly once; clamped duplicate loads past a range are not counted).
+// Thread gid writes its XOR to out[gid], so XOR-ing out gives the XOR of the
+// whole buffer.
+__global__ __launch_bounds__(kProbeThreads) void read_probe_kernel(const u32x4* __restrict__ buf,
+                                                                 int64_t nchunk,
+                                                                 u32x4* __restrict__ out) {
+    constexpr int U = 2;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t nw = (int64_t)gridDim.x * (kProbeThreads / 64);
+    const int64_t gw = (int64_t)blockIdx.x * (kProbeThreads / 64) + wave;
+    const int64_t base = nchunk / nw, rem = nchunk % nw;
+    const int64_t s = gw * base + min(gw, rem);
+    const int64_t len = base + (gw < rem ? 1 : 0);
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    if (len > 0) {
+        const u32x4* p = buf + s * 64 + lane;
+        u32x4 a[U], b[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) a[u] = __builtin_nontemporal_load(p + min((int64_t)u, len - 1) * 64);
+        for (int64_t i = 0; i < len; i += 2 * U) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                b[u] = __builtin_nontemporal_load(p + min(i + U + u, len - 1) * 64);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (i + u < len) acc ^= a[u];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                a[u] = __builtin_nontemporal_load(p + min(i + 2 * U + u, len - 1) * 64);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (i + U + u < len) acc ^= b[u];
+        }
+    }
+    out[(int64_t)blockIdx.x * kProbeThreads + threadIdx.x] = acc;
+}
+
+hipError_t launch_read_probe(const void* buf, size_t bytes, void* out, hipStream_t stream) {
+    hipLaunchKernelGGL(read_probe_kernel, dim3(kProbeBlocks), dim3(kProbeThreads), 0, stream,
+                       (const u32x4*)buf, (int64_t)(bytes / kChunkBytes), (u32x4*)out);
+    return hipGetLastError();
+}
+
 hipError_t launch_mfma_probe(const void* A, const void* B, float* D, bool bf16,
                              hipStream_t stream) {
     if (bf16)

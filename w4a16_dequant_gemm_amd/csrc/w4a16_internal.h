@@ -70,6 +70,10 @@ W4A16_DECLARE_GEMM_PART(launch_gemm_f16_ep)
 W4A16_DECLARE_GEMM_PART(launch_gemm_bf16)
 W4A16_DECLARE_GEMM_PART(launch_gemm_bf16_ep)
 #undef W4A16_DECLARE_GEMM_PART
+// Read-bandwidth probe geometry: one workgroup of 8 waves per CU.
+constexpr int kProbeBlocks = 256;
+constexpr int kProbeThreads = 512;
+hipError_t launch_read_probe(const void* buf, size_t bytes, void* out, hipStream_t stream);
 hipError_t launch_mfma_probe(const void* A, const void* B, float* D, bool bf16,
                              hipStream_t stream);
 
