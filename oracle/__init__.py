@@ -139,6 +139,17 @@ def dequant_values(q, z, s_bits, dtype):
     return out
 
 
+def _threads(n):
+    """Worker threads: n if given, else this process's CPU share, at most 16."""
+    if n and n > 0:
+        return int(n)
+    try:
+        share = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        share = os.cpu_count() or 1
+    return max(1, min(16, share))
+
+
 def gemm(X, qweight, scales, zeros, M, N, K, G, dtype, sym, with_exact=False, nthreads=0):
     """(Y, B) or (Y, B, Yx): fp64 [M][N] product, error-bound denominator, unrounded-deq product."""
     x = _c(X, np.uint16)
@@ -150,7 +161,7 @@ def gemm(X, qweight, scales, zeros, M, N, K, G, dtype, sym, with_exact=False, nt
     Yx = np.empty((M, N), dtype=np.float64) if with_exact else None
     code = dtype_code(dtype) if isinstance(dtype, str) else dtype
     rc = _load().oracle_gemm(_ptr(x), _ptr(qw), _ptr(sc), _ptr(zr), M, N, K, G, code,
-                             int(bool(sym)), _ptr(Y), _ptr(B), _ptr(Yx), int(nthreads))
+                             int(bool(sym)), _ptr(Y), _ptr(B), _ptr(Yx), _threads(nthreads))
     if rc:
         raise ValueError(f"oracle_gemm failed with status {rc}")
     return (Y, B, Yx) if with_exact else (Y, B)
@@ -170,7 +181,7 @@ def gemm_at(X, qweight, scales, zeros, M, N, K, G, dtype, sym, ms, ns, nthreads=
     code = dtype_code(dtype) if isinstance(dtype, str) else dtype
     rc = _load().oracle_gemm_at(_ptr(x), _ptr(qw), _ptr(sc), _ptr(zr), M, N, K, G, code,
                                 int(bool(sym)), _ptr(ms), _ptr(ns), ms.size, _ptr(Y),
-                                _ptr(B), int(nthreads))
+                                _ptr(B), _threads(nthreads))
     if rc:
         raise ValueError(f"oracle_gemm_at failed with status {rc}")
     return Y, B

@@ -308,3 +308,26 @@ def test_read_probe_reads_every_byte_once(nbytes):
     got = np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32).reshape(-1, 4), axis=0)
     want = np.bitwise_xor.reduce(host.reshape(-1, 4), axis=0)
     assert np.array_equal(got, want)
+
+
+PREFILL = [n for n in synth.WORKLOADS if n.startswith("prefill_")]
+
+
+@pytest.mark.parametrize("name", PREFILL)
+def test_prefill_dense_samples(name):
+    """Prefill at full size in the benchmark's launch configuration: 8 random
+    rows over every output column and every row over 32 random columns,
+    against the oracle element by element."""
+    p = full_problem(name)
+    say(f"prefill dense samples {name}: M={p.M} K={p.K} N={p.N}")
+    d = OnDevice(p)
+    Y = d.gemm()
+    Yf = d.y_float(Y)
+    rng = np.random.default_rng(7)
+    rows = rng.choice(p.M, 8, replace=False)
+    cols = rng.choice(p.N, 32, replace=False)
+    ms = np.concatenate([np.repeat(rows, p.N), np.tile(np.arange(p.M), 32)])
+    ns = np.concatenate([np.tile(np.arange(p.N), 8), np.repeat(cols, p.M)])
+    Yref, B = oracle.gemm_at(p.X, p.qweight, p.scales, p.zeros, p.M, p.N, p.K, p.G, p.dtype,
+                             p.sym, ms, ns)
+    assert_gemm_close(p, Yf[ms, ns], Yref, B, name)
