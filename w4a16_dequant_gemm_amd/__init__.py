@@ -114,10 +114,33 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _stream(stream) -> ctypes.c_void_p:
+def _stream_handle(stream) -> int:
+    """hipStream_t of `stream` (a torch stream, a raw handle, or None = torch's
+    current stream on the current device) as an integer."""
     if stream is None:
         stream = torch.cuda.current_stream()
-    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    return ctypes.c_void_p(_stream_handle(stream))
+
+
+def _bad(where: str):
+    raise W4A16Error(W4A16_ERR_INVALID_ARG, where)
+
+
+def _require(t: Optional[torch.Tensor], where: str, dtype, numel: int, device=None):
+    """A device tensor of the given dtype and element count, contiguous, on
+    `device` when given: the checks the C entry points cannot make themselves
+    (they see only pointers), so an undersized buffer never reaches a kernel."""
+    if t is None:
+        _bad(f"{where}: missing")
+    if (t.dtype != dtype or t.numel() != numel or not t.is_contiguous() or not t.is_cuda
+            or (device is not None and t.device != device)):
+        _bad(f"{where}: need a contiguous {dtype} device tensor of {numel} elements"
+             f"{'' if device is None else ' on ' + str(device)}, got {t.dtype} "
+             f"{tuple(t.shape)} on {t.device}")
 
 
 def flags_of(dtype: str, sym: bool) -> int:
@@ -171,11 +194,23 @@ class PackedW4:
 
 def w4a16_repack(qweight: torch.Tensor, scales: torch.Tensor, zeros: Optional[torch.Tensor],
                  K: int, N: int, group_size: int, flags: int, stream=None) -> PackedW4:
+    """Canonical qweight int32/uint32-bits [K/8][N], scales [K/G][N] (fp16 or bf16 per
+    flags) and zeros uint8 [K/G][N] (None for the symmetric format) -> PackedW4."""
     nbytes = w4a16_packed_bytes(K, N, group_size, flags)
     if nbytes == 0:
         raise W4A16Error(W4A16_ERR_UNSUPPORTED if N % 128 else W4A16_ERR_INVALID_ARG,
                          "w4a16_packed_bytes")
-    packed = torch.empty(nbytes, dtype=torch.uint8, device=qweight.device)
+    dev = qweight.device
+    if qweight.dtype not in (torch.int32, torch.uint32) or qweight.numel() != (K // 8) * N \
+            or not qweight.is_contiguous() or not qweight.is_cuda:
+        _bad("w4a16_repack: qweight must be a contiguous int32 device tensor of K/8*N elements")
+    _require(scales, "w4a16_repack: scales", torch_dtype(flags), (K // group_size) * N, dev)
+    if flags & W4A16_SYM:
+        if zeros is not None:
+            _bad("w4a16_repack: the symmetric format takes no zeros")
+    else:
+        _require(zeros, "w4a16_repack: zeros", torch.uint8, (K // group_size) * N, dev)
+    packed = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     _check(load_library().w4a16_repack(_ptr(qweight), _ptr(scales), _ptr(zeros), K, N,
                                        group_size, flags, _ptr(packed), nbytes, _stream(stream)),
            "w4a16_repack")
@@ -194,20 +229,68 @@ def w4a16_unrepack(packed: PackedW4, stream=None):
     return qweight, scales, zeros
 
 
+# Workspaces cached per (device, stream): calls on different streams may run
+# concurrently and must not share counters or partial tiles.  A workspace
+# that has to grow is replaced, and the old one is kept alive for the rest of
+# the process: a kernel still running on its stream, or a captured graph, may
+# hold its address.
 _workspaces = {}
+_retired_workspaces = []
 
 
-def workspace_for(nbytes: int, device: torch.device) -> Optional[torch.Tensor]:
-    """A zero-filled workspace of at least nbytes, cached per device (the library
-    leaves its counters zero after every call)."""
+def workspace_for(nbytes: int, device: torch.device, stream=None) -> Optional[torch.Tensor]:
+    """A zero-filled workspace of at least nbytes for calls on `stream` (default:
+    torch's current stream) on `device`.  The library leaves its counters zero
+    after every call, so the buffer is reused as it is."""
     if nbytes == 0:
         return None
-    key = (device.type, device.index)
+    key = (device.type, device.index, _stream_handle(stream))
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        size = 1 << 20
+        while size < nbytes:
+            size *= 2
+        if ws is not None:
+            _retired_workspaces.append(ws)
+        ws = torch.zeros(size, dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
+
+
+def _gemm_args(where, X, packed, M, Y, col_scale=None, bias=None, aux=None, activation="none",
+               aux_op="add"):
+    """Checks of the tensor arguments of the GEMM entry points; returns (M, Y, ep)
+    with Y allocated if not given and ep the w4a16_epilogue_t (None if no
+    epilogue operand or activation is given)."""
+    if packed.layout_version != _layout_version:
+        _bad(f"{where}: blob layout version {packed.layout_version}, library {_layout_version}")
+    K, N, flags = packed.K, packed.N, packed.flags
+    if M is None:
+        M = X.shape[0]
+    dt = torch_dtype(flags)
+    _require(X, f"{where}: X", dt, M * K)
+    dev = X.device
+    if packed.data.device != dev:
+        _bad(f"{where}: the blob is on {packed.data.device}, X on {dev}")
+    if Y is None:
+        Y = torch.empty((M, N), dtype=dt, device=dev)
+    else:
+        _require(Y, f"{where}: Y", dt, M * N, dev)
+    if col_scale is not None:
+        _require(col_scale, f"{where}: col_scale", torch.float32, N, dev)
+    if bias is not None:
+        _require(bias, f"{where}: bias", dt, N, dev)
+    if aux is not None:
+        _require(aux, f"{where}: aux", dt, M * N, dev)
+    if activation not in W4A16_ACT or aux_op not in W4A16_AUX:
+        _bad(f"{where}: activation {activation!r} / aux_op {aux_op!r}")
+    ep = None
+    if col_scale is not None or bias is not None or aux is not None or activation != "none":
+        ep = Epilogue(None if col_scale is None else col_scale.data_ptr(),
+                      None if bias is None else bias.data_ptr(),
+                      None if aux is None else aux.data_ptr(), W4A16_ACT[activation],
+                      W4A16_AUX[aux_op])
+    return M, Y, ep
 
 
 def w4a16_gemm(X: torch.Tensor, packed: PackedW4, M: Optional[int] = None,
@@ -215,17 +298,10 @@ def w4a16_gemm(X: torch.Tensor, packed: PackedW4, M: Optional[int] = None,
                stream=None) -> torch.Tensor:
     """Y[M][N] = X[M][K] . dequant(packed); X is [M][K] fp16/bf16 on the device."""
     lib = load_library()
-    if packed.layout_version != _layout_version:
-        raise W4A16Error(W4A16_ERR_INVALID_ARG, "w4a16_gemm (blob layout version)")
+    M, Y, _ = _gemm_args("w4a16_gemm", X, packed, M, Y)
     K, N, G, flags = packed.K, packed.N, packed.group_size, packed.flags
-    if M is None:
-        M = X.shape[0]
-    if X.dtype != torch_dtype(flags) or X.numel() != M * K or not X.is_contiguous():
-        raise W4A16Error(W4A16_ERR_INVALID_ARG, "w4a16_gemm (X dtype/shape)")
-    if Y is None:
-        Y = torch.empty((M, N), dtype=X.dtype, device=X.device)
     if workspace is None:
-        workspace = workspace_for(_workspace_need(M, N, K, G, flags), X.device)
+        workspace = workspace_for(_workspace_need(M, N, K, G, flags), X.device, stream)
     _check(lib.w4a16_gemm(_ptr(X), _ptr(packed.data), packed.data.numel(), _ptr(Y), M, N, K, G,
                           flags, _ptr(workspace), 0 if workspace is None else workspace.numel(),
                           _stream(stream)), "w4a16_gemm")
@@ -241,31 +317,13 @@ def w4a16_gemm_ex(X: torch.Tensor, packed: PackedW4, M: Optional[int] = None,
     Y = aux_op(act(X.deq * col_scale + bias), aux): col_scale fp32 [N], bias [N]
     and aux [M][N] in X's dtype, each optional (device tensors)."""
     lib = load_library()
-    if packed.layout_version != _layout_version:
-        raise W4A16Error(W4A16_ERR_INVALID_ARG, "w4a16_gemm_ex (blob layout version)")
+    M, Y, ep = _gemm_args("w4a16_gemm_ex", X, packed, M, Y, col_scale, bias, aux, activation,
+                          aux_op)
     K, N, G, flags = packed.K, packed.N, packed.group_size, packed.flags
-    if M is None:
-        M = X.shape[0]
-    if X.dtype != torch_dtype(flags) or X.numel() != M * K or not X.is_contiguous():
-        raise W4A16Error(W4A16_ERR_INVALID_ARG, "w4a16_gemm_ex (X dtype/shape)")
-    if col_scale is not None and (col_scale.dtype != torch.float32 or col_scale.numel() != N
-                                  or not col_scale.is_contiguous()):
-        raise W4A16Error(W4A16_ERR_INVALID_ARG, "w4a16_gemm_ex (col_scale)")
-    for name, t, n in (("bias", bias, N), ("aux", aux, M * N)):
-        if t is not None and (t.dtype != X.dtype or t.numel() != n or not t.is_contiguous()):
-            raise W4A16Error(W4A16_ERR_INVALID_ARG, f"w4a16_gemm_ex ({name})")
-    if activation not in W4A16_ACT or aux_op not in W4A16_AUX:
-        raise W4A16Error(W4A16_ERR_INVALID_ARG, "w4a16_gemm_ex (activation/aux_op)")
-    if Y is None:
-        Y = torch.empty((M, N), dtype=X.dtype, device=X.device)
     if workspace is None:
-        workspace = workspace_for(_workspace_need(M, N, K, G, flags), X.device)
-    ep = Epilogue(None if col_scale is None else col_scale.data_ptr(),
-                  None if bias is None else bias.data_ptr(),
-                  None if aux is None else aux.data_ptr(), W4A16_ACT[activation],
-                  W4A16_AUX[aux_op])
+        workspace = workspace_for(_workspace_need(M, N, K, G, flags), X.device, stream)
     _check(lib.w4a16_gemm_ex(_ptr(X), _ptr(packed.data), packed.data.numel(), _ptr(Y), M, N, K,
-                             G, flags, ctypes.byref(ep), _ptr(workspace),
+                             G, flags, None if ep is None else ctypes.byref(ep), _ptr(workspace),
                              0 if workspace is None else workspace.numel(), _stream(stream)),
            "w4a16_gemm_ex")
     return Y

@@ -15,10 +15,10 @@ namespace {
 
 constexpr int kNumCUs = 256;        // MI355X compute units
 constexpr int kMaxSplits = 16;
-// Counter area at the start of every workspace: one uint32 per output tile,
-// at a fixed size for every shape, so the partial sums of one call can never
-// land where another call's counters live when callers share a workspace.
-constexpr size_t kCounterBytes = 64 * 1024;
+// One uint32 counter per output tile in the workspace's counter area, which
+// has the same size (kCounterBytes) for every shape, so the partial sums of
+// one call never land where another call's counters live when calls share a
+// workspace.
 constexpr int kMaxTilesSplit = (int)(kCounterBytes / 4);
 constexpr int64_t kMaxDim = (int64_t)1 << 31;
 
@@ -163,6 +163,55 @@ hipError_t launch_gemm(const void* X, const void* packed, void* Y, int64_t M, co
                   : launch_gemm_f16(X, packed, Y, M, L, plan, workspace, ep, stream);
 }
 
+w4a16_status_t prepare_gemm(const void* X, const void* packed, size_t packed_bytes, void* Y,
+                            int64_t M, int64_t N, int64_t K, int group_size, uint32_t flags,
+                            const w4a16_epilogue_t* epilogue, GemmCall* out) {
+    if (M < 1 || M >= kMaxDim) return W4A16_ERR_INVALID_ARG;
+    w4a16_status_t st = check_shape(K, N, group_size, flags);
+    if (st != W4A16_OK) return st;
+    if (!X || !packed || !Y) return W4A16_ERR_INVALID_ARG;
+    if (!aligned16(X) || !aligned16(packed) || !aligned16(Y)) return W4A16_ERR_INVALID_ARG;
+    if ((double)M * (double)K >= (double)((int64_t)1 << 40) ||
+        (double)M * (double)N >= (double)((int64_t)1 << 40))
+        return W4A16_ERR_INVALID_ARG;
+    Epilogue& ep = out->ep;
+    memset(&ep, 0, sizeof(ep));
+    if (epilogue) {
+        const w4a16_epilogue_t& e = *epilogue;
+        if (e.activation < W4A16_ACT_NONE || e.activation > W4A16_ACT_SILU) return W4A16_ERR_INVALID_ARG;
+        if (e.aux_op != W4A16_AUX_ADD && e.aux_op != W4A16_AUX_MUL) return W4A16_ERR_INVALID_ARG;
+        if (((uintptr_t)e.col_scale & 3) || ((uintptr_t)e.bias & 1) || ((uintptr_t)e.aux & 1))
+            return W4A16_ERR_INVALID_ARG;
+        if (e.aux && e.aux != Y) {   // aux is Y itself (in place) or disjoint from it
+            const uintptr_t a0 = (uintptr_t)e.aux, y0 = (uintptr_t)Y;
+            const uintptr_t bytes = (uintptr_t)(M * N * 2);
+            if (a0 < y0 + bytes && y0 < a0 + bytes) return W4A16_ERR_INVALID_ARG;
+        }
+        // absent operands read harmless memory of at least their size: the
+        // blob (>= K*N/2 >= 16*N bytes) for [N] operands, Y for [M][N]
+        ep.has_scale = e.col_scale != nullptr;
+        ep.has_bias = e.bias != nullptr;
+        ep.has_aux = e.aux != nullptr;
+        ep.col_scale = e.col_scale ? e.col_scale : (const float*)packed;
+        ep.bias = (const uint16_t*)(e.bias ? e.bias : packed);
+        ep.aux = (const uint16_t*)(e.aux ? e.aux : Y);
+        ep.act = e.activation;
+        ep.aux_mul = e.aux_op == W4A16_AUX_MUL;
+        ep.any = ep.has_scale || ep.has_bias || ep.has_aux || e.activation != W4A16_ACT_NONE;
+    }
+    out->layout = make_layout(K, N, group_size, (flags & W4A16_SYM) != 0);
+    if (packed_bytes < out->layout.total) return W4A16_ERR_INVALID_ARG;
+    out->plan = make_plan(M, N, K, group_size, flags);
+    out->bf16 = (flags & W4A16_BF16) != 0;
+    return W4A16_OK;
+}
+
+w4a16_status_t run_gemm(const GemmCall& c, const void* X, const void* packed, void* Y, int64_t M,
+                        void* workspace, hipStream_t stream) {
+    return from_hip(launch_gemm(X, packed, Y, M, c.layout, c.bf16, c.plan, workspace, c.ep,
+                                stream));
+}
+
 }  // namespace w4a16
 
 using namespace w4a16;
@@ -232,48 +281,15 @@ w4a16_status_t w4a16_gemm_ex(const void* X, const void* packed, size_t packed_by
                              int64_t M, int64_t N, int64_t K, int group_size, uint32_t flags,
                              const w4a16_epilogue_t* epilogue, void* workspace,
                              size_t workspace_bytes, void* stream) {
-    if (M < 1 || M >= kMaxDim) return W4A16_ERR_INVALID_ARG;
-    w4a16_status_t st = check_shape(K, N, group_size, flags);
+    GemmCall c;
+    const w4a16_status_t st =
+        prepare_gemm(X, packed, packed_bytes, Y, M, N, K, group_size, flags, epilogue, &c);
     if (st != W4A16_OK) return st;
-    if (!X || !packed || !Y) return W4A16_ERR_INVALID_ARG;
-    if (!aligned16(X) || !aligned16(packed) || !aligned16(Y)) return W4A16_ERR_INVALID_ARG;
-    if ((double)M * (double)K >= (double)((int64_t)1 << 40) ||
-        (double)M * (double)N >= (double)((int64_t)1 << 40))
-        return W4A16_ERR_INVALID_ARG;
-    Epilogue ep;
-    memset(&ep, 0, sizeof(ep));
-    if (epilogue) {
-        const w4a16_epilogue_t& e = *epilogue;
-        if (e.activation < W4A16_ACT_NONE || e.activation > W4A16_ACT_SILU) return W4A16_ERR_INVALID_ARG;
-        if (e.aux_op != W4A16_AUX_ADD && e.aux_op != W4A16_AUX_MUL) return W4A16_ERR_INVALID_ARG;
-        if (((uintptr_t)e.col_scale & 3) || ((uintptr_t)e.bias & 1) || ((uintptr_t)e.aux & 1))
-            return W4A16_ERR_INVALID_ARG;
-        if (e.aux && e.aux != Y) {   // aux is Y itself (in place) or disjoint from it
-            const uintptr_t a0 = (uintptr_t)e.aux, y0 = (uintptr_t)Y;
-            const uintptr_t bytes = (uintptr_t)(M * N * 2);
-            if (a0 < y0 + bytes && y0 < a0 + bytes) return W4A16_ERR_INVALID_ARG;
-        }
-        // absent operands read harmless memory of at least their size: the
-        // blob (>= K*N/2 >= 16*N bytes) for [N] operands, Y for [M][N]
-        ep.has_scale = e.col_scale != nullptr;
-        ep.has_bias = e.bias != nullptr;
-        ep.has_aux = e.aux != nullptr;
-        ep.col_scale = e.col_scale ? e.col_scale : (const float*)packed;
-        ep.bias = (const uint16_t*)(e.bias ? e.bias : packed);
-        ep.aux = (const uint16_t*)(e.aux ? e.aux : Y);
-        ep.act = e.activation;
-        ep.aux_mul = e.aux_op == W4A16_AUX_MUL;
-        ep.any = ep.has_scale || ep.has_bias || ep.has_aux || e.activation != W4A16_ACT_NONE;
-    }
-    const Layout L = make_layout(K, N, group_size, (flags & W4A16_SYM) != 0);
-    if (packed_bytes < L.total) return W4A16_ERR_INVALID_ARG;
-    const Plan plan = make_plan(M, N, K, group_size, flags);
-    if (plan.workspace > 0) {
-        if (!workspace || workspace_bytes < plan.workspace || !aligned16(workspace))
+    if (c.plan.workspace > 0) {
+        if (!workspace || workspace_bytes < c.plan.workspace || !aligned16(workspace))
             return W4A16_ERR_WORKSPACE;
     }
-    return from_hip(launch_gemm(X, packed, Y, M, L, (flags & W4A16_BF16) != 0, plan, workspace,
-                                ep, (hipStream_t)stream));
+    return run_gemm(c, X, packed, Y, M, workspace, (hipStream_t)stream);
 }
 
 w4a16_status_t w4a16_gemm(const void* X, const void* packed, size_t packed_bytes, void* Y,

@@ -5,6 +5,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/w4a16.h"
 #include "w4a16_layout.h"
 
 namespace w4a16 {
@@ -70,6 +71,24 @@ W4A16_DECLARE_GEMM_PART(launch_gemm_f16_ep)
 W4A16_DECLARE_GEMM_PART(launch_gemm_bf16)
 W4A16_DECLARE_GEMM_PART(launch_gemm_bf16_ep)
 #undef W4A16_DECLARE_GEMM_PART
+// One validated w4a16_gemm_ex request: the blob layout, the plan and the
+// epilogue.  prepare_gemm checks every argument on the host (no HIP call);
+// run_gemm launches the kernels with the given workspace (which must hold at
+// least plan.workspace bytes when that is nonzero).
+struct GemmCall {
+    Layout layout;
+    Plan plan;
+    Epilogue ep;
+    bool bf16;
+};
+w4a16_status_t prepare_gemm(const void* X, const void* packed, size_t packed_bytes, void* Y,
+                            int64_t M, int64_t N, int64_t K, int group_size, uint32_t flags,
+                            const w4a16_epilogue_t* epilogue, GemmCall* out);
+w4a16_status_t run_gemm(const GemmCall& c, const void* X, const void* packed, void* Y, int64_t M,
+                        void* workspace, hipStream_t stream);
+// Byte size of the counter area at the start of every workspace (the same
+// for every shape).
+constexpr size_t kCounterBytes = 64 * 1024;
 // Read-bandwidth probe geometry: one workgroup of 8 waves per CU.
 constexpr int kProbeBlocks = 256;
 constexpr int kProbeThreads = 512;

@@ -32,8 +32,8 @@
 //
 // Trailer (16 bytes, after region Z): uint32 magic kTrailerMagic, uint32 layout
 // version, uint32 feature flags, uint32 group size.  Feature flag
-// kFlagExactBf16 is set by the repack when some column's -z*s overflows fp32
-// (bf16 scales above about 2.3e37); the GEMM kernels then use the exact
+// kFlagExactBf16 is set by the repack when some column's -(1024+z)*s overflows
+// fp32 (bf16 scales above about 3.3e35); the GEMM kernels then use the exact
 // dequant form for the whole launch instead of testing every group.
 #pragma once
 #include <stddef.h>
