@@ -187,6 +187,34 @@ w4a16_status_t w4a16_gemm_ex(const void *X, const void *packed, size_t packed_by
                              size_t workspace_bytes, void *stream);
 
 /*
+ * Size of the device scratch array behind w4a16_gemm_noalloc: 16 MiB per GPU
+ * the library runs on, held until the process ends.
+ */
+#define W4A16_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/*
+ * w4a16_gemm_ex for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments without the workspace.  The kernels' scratch (cross-
+ * workgroup counters and fp32 partial tiles) lives in a static device array of
+ * W4A16_NOALLOC_SCRATCH_BYTES per GPU instead.  The call allocates nothing
+ * and frees nothing.  The caller still provides X, packed and Y.
+ *   - The first call on a GPU looks up that GPU's array and enqueues one small
+ *     kernel on `stream` that zeroes its counter area; every call leaves the
+ *     counters zero again.
+ *   - Every call on one GPU shares that GPU's array: calls that may overlap in
+ *     time on one GPU (different streams, or concurrent host threads) race and
+ *     can return wrong results.  Serialize them (one stream, or events).
+ * Errors: those of w4a16_gemm_ex, and W4A16_ERR_WORKSPACE when the shape needs
+ * more scratch than W4A16_NOALLOC_SCRATCH_BYTES (w4a16_workspace_bytes() tells
+ * how much it needs); nothing is launched then.
+ */
+w4a16_status_t w4a16_gemm_noalloc(const void *X, const void *packed, size_t packed_bytes,
+                                  void *Y, int64_t M, int64_t N, int64_t K, int group_size,
+                                  uint32_t flags, const w4a16_epilogue_t *epilogue,
+                                  void *stream);
+
+/*
  * Test and export aid: writes deq[K][N] row-major (activation dtype) from a
  * blob, using the same device dequantization code as w4a16_gemm.  This is the
  * materialising "route B" the fused path avoids (page "量化开销对比",

@@ -177,3 +177,18 @@ def test_product_package_never_imports_the_oracle():
                 text = open(os.path.join(dirpath, f), encoding="utf-8").read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "w4a16_oracle" not in text and "liboracle" not in text, f
+
+
+def test_noalloc_rejects_before_any_launch(lib):
+    """w4a16_gemm_noalloc validates like w4a16_gemm_ex and refuses a shape whose
+    plan needs more scratch than its static array, before any HIP call."""
+    def call(X=FAKE, packed=FAKE, pbytes=1 << 40, Y=FAKE, M=8, N=4096, K=4096, G=128, flags=0):
+        return lib.w4a16_gemm_noalloc(X, packed, pbytes, Y, M, N, K, G, flags, None, None)
+    M, N, K, G = 128, 28672, 8192, 64
+    assert w4.w4a16_workspace_bytes(M, N, K, G, 0) > w4.W4A16_NOALLOC_SCRATCH_BYTES
+    assert call(M=M, N=N, K=K, G=G) == w4.W4A16_ERR_WORKSPACE
+    assert call(M=0) == w4.W4A16_ERR_INVALID_ARG
+    assert call(X=NULL) == w4.W4A16_ERR_INVALID_ARG
+    assert call(Y=FAKE_MIS) == w4.W4A16_ERR_INVALID_ARG
+    assert call(N=4000) == w4.W4A16_ERR_UNSUPPORTED
+    assert call(pbytes=100) == w4.W4A16_ERR_INVALID_ARG

@@ -35,7 +35,9 @@ C_FUNCTIONS = (
     "w4a16_abi_version", "w4a16_layout_version", "w4a16_status_string", "w4a16_packed_bytes",
     "w4a16_repack", "w4a16_unrepack", "w4a16_workspace_bytes", "w4a16_gemm", "w4a16_dequant",
     "w4a16_mfma_layout_probe", "w4a16_gemm_ex", "w4a16_read_probe", "w4a16_read_probe_out_bytes",
+    "w4a16_gemm_noalloc",
 )
+W4A16_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class W4A16Error(RuntimeError):
@@ -87,6 +89,9 @@ def load_library(path: str = LIB_PATH):
     lib.w4a16_gemm_ex.argtypes = [p, p, sz, p, i64, i64, i64, ci, u32, ctypes.POINTER(Epilogue), p,
                                   sz, p]
     lib.w4a16_gemm_ex.restype = ci
+    lib.w4a16_gemm_noalloc.argtypes = [p, p, sz, p, i64, i64, i64, ci, u32,
+                                       ctypes.POINTER(Epilogue), p]
+    lib.w4a16_gemm_noalloc.restype = ci
     lib.w4a16_dequant.argtypes = [p, sz, p, i64, i64, ci, u32, p]
     lib.w4a16_dequant.restype = ci
     lib.w4a16_mfma_layout_probe.argtypes = [p, p, p, u32, p]
@@ -326,6 +331,26 @@ def w4a16_gemm_ex(X: torch.Tensor, packed: PackedW4, M: Optional[int] = None,
                              G, flags, None if ep is None else ctypes.byref(ep), _ptr(workspace),
                              0 if workspace is None else workspace.numel(), _stream(stream)),
            "w4a16_gemm_ex")
+    return Y
+
+
+def w4a16_gemm_noalloc(X: torch.Tensor, packed: PackedW4, Y: torch.Tensor,
+                       M: Optional[int] = None, stream=None, *,
+                       col_scale: Optional[torch.Tensor] = None,
+                       bias: Optional[torch.Tensor] = None, aux: Optional[torch.Tensor] = None,
+                       activation: str = "none", aux_op: str = "add") -> torch.Tensor:
+    """w4a16_gemm_ex without a workspace: the library's static per-GPU scratch
+    (W4A16_NOALLOC_SCRATCH_BYTES) serves instead, and nothing is allocated.
+    The caller provides Y.  Calls that may overlap in time on one GPU race."""
+    if Y is None:
+        _bad("w4a16_gemm_noalloc: Y must be provided")
+    lib = load_library()
+    M, Y, ep = _gemm_args("w4a16_gemm_noalloc", X, packed, M, Y, col_scale, bias, aux,
+                          activation, aux_op)
+    _check(lib.w4a16_gemm_noalloc(_ptr(X), _ptr(packed.data), packed.data.numel(), _ptr(Y), M,
+                                  packed.N, packed.K, packed.group_size, packed.flags,
+                                  None if ep is None else ctypes.byref(ep), _stream(stream)),
+           "w4a16_gemm_noalloc")
     return Y
 
 

@@ -27,6 +27,7 @@ COMMON = [
 UNITS = [
     ("w4a16_api.cpp", []),
     ("w4a16_repack.hip", []),
+    ("w4a16_noalloc.hip", []),
     ("w4a16_gemm.hip", ["-DW4A16_TU_BF16=0", "-DW4A16_TU_EP=0"]),
     ("w4a16_gemm.hip", ["-DW4A16_TU_BF16=1", "-DW4A16_TU_EP=0"]),
     ("w4a16_gemm.hip", ["-DW4A16_TU_BF16=0", "-DW4A16_TU_EP=1"]),
