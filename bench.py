@@ -153,7 +153,8 @@ def measured_traffic(name):
     return int(rec["traffic_bytes"])
 
 
-def run_workload(name, steps, warmup, rotate_bytes=1 << 30, with_cpu=True, comparators=True):
+def run_workload(name, steps, warmup, rotate_bytes=1 << 30, with_cpu=True, comparators=True,
+                 plan=None):
     import torch
 
     import w4a16_dequant_gemm_amd as w4
@@ -170,12 +171,13 @@ def run_workload(name, steps, warmup, rotate_bytes=1 << 30, with_cpu=True, compa
     blobs = [base] + [w4.PackedW4(base.data.clone(), base.K, base.N, base.group_size, base.flags,
                                   base.layout_version) for _ in range(copies - 1)]
     Y = torch.empty((p.M, p.N), dtype=X.dtype, device=dev)
-    ws = w4.workspace_for(w4.w4a16_workspace_bytes(p.M, p.N, p.K, p.G, flags), dev)
+    ws_bytes = w4.w4a16_workspace_bytes(p.M, p.N, p.K, p.G, flags | w4.plan_flags(plan))
+    ws = None if ws_bytes == 0 else torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     def step(i):
         # the current stream: the default one, or the capture stream below
-        w4.w4a16_gemm(X, blobs[i % copies], Y=Y, workspace=ws)
+        w4.w4a16_gemm(X, blobs[i % copies], Y=Y, workspace=ws, plan=plan)
 
     for i in range(warmup):
         step(i)
@@ -275,6 +277,7 @@ def run_workload(name, steps, warmup, rotate_bytes=1 << 30, with_cpu=True, compa
         "dtype": "f16" if p.dtype == "fp16" else "bf16",
         "data": "synthetic",
         "config": {"workload": name, "M": p.M, "K": p.K, "N": p.N, "group_size": p.G,
+                   "plan": plan,
                    "act_dtype": p.dtype, "quant": "sym" if p.sym else "asym",
                    "outlier_cols": cfg.get("outlier_frac", 0.0), "parallelism": "none (1 GPU)",
                    "cold_weight_copies": copies, "launch": "hip_graph_replay"},
@@ -444,6 +447,9 @@ def main():
                          "one of " + ", ".join(LAYER_WORKLOADS) + " (fused FFN block)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-comparators", action="store_true")
+    ap.add_argument("--plan", default=None,
+                    help="kernel hint, e.g. decode, decode:2, splitk, tiled:4 (default: the "
+                         "library's own choice)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="before the workload, run a plain device copy of this many MiB (a "
                          "known-size kernel for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -464,11 +470,15 @@ def main():
     if args.workload.startswith(LAYER_PREFIX):
         print(json.dumps(run_ffn_layer(args.workload, args.steps, args.warmup)), flush=True)
         return
-    names = list(synth.WORKLOADS) if args.workload == "all" else [args.workload]
+    plan = None
+    if args.plan:
+        name_, _, param = args.plan.partition(":")
+        plan = (name_, int(param or 0))
+    names = list(synth.WORKLOADS) if args.workload == "all" else args.workload.split(",")
     for name in names:
         out = run_workload(name, args.steps, args.warmup,
-                           with_cpu=not args.no_cpu and args.workload != "all",
-                           comparators=not args.no_comparators)
+                           with_cpu=not args.no_cpu and len(names) == 1,
+                           comparators=not args.no_comparators, plan=plan)
         print(json.dumps(out), flush=True)
 
 

@@ -24,9 +24,9 @@
  *   - Every argument is validated on the host before any HIP call.  A call
  *     that fails validation launches nothing and writes nothing.  A launch
  *     error reported by HIP is returned as W4A16_ERR_HIP.
- *   - Supported shapes: M >= 1; K >= 1 with K % G == 0; N >= 1 with N % 128 == 0
- *     (other N: W4A16_ERR_UNSUPPORTED); G in {32, 64, 128} (other G:
- *     W4A16_ERR_UNSUPPORTED); M, N, K < 2^31 and K*N < 2^40.
+ *   - Supported shapes: M >= 1; K >= 1 with K % G == 0 and K % 256 == 0; N >= 1
+ *     with N % 128 == 0 (other K or N: W4A16_ERR_UNSUPPORTED); G in {32, 64,
+ *     128} (other G: W4A16_ERR_UNSUPPORTED); M, N, K < 2^31 and K*N < 2^40.
  *   - Every dev pointer must be 16-byte aligned.
  */
 #ifndef W4A16_H
@@ -40,7 +40,7 @@ extern "C" {
 #endif
 
 #define W4A16_ABI_VERSION 1
-#define W4A16_LAYOUT_VERSION 1
+#define W4A16_LAYOUT_VERSION 2
 
 typedef enum {
     W4A16_OK = 0,
@@ -56,6 +56,24 @@ typedef enum {
 #define W4A16_ASYM 0x0u   /* zeros: uint8 [K/G][N], values 0..15 */
 #define W4A16_SYM  0x2u   /* zero point fixed at 8; the zeros pointer must be NULL */
 #define W4A16_FLAGS_MASK 0x3u
+
+/*
+ * Plan hints, OR-ed into the flags of w4a16_workspace_bytes and the GEMM
+ * calls only (never into a blob's flags): force one kernel variant, for
+ * benchmarks and tests.  Give the same flags to w4a16_workspace_bytes and to
+ * the GEMM call.  A hint that does not apply to the shape is ignored (the
+ * default choice is made).  W4A16_PLAN_PARAM(n), n in 1..255, sets the
+ * variant's parameter: the decode kernel's workgroup count (at most one per
+ * output tile), split-K workgroups in units of 8, or the tiled kernel's split
+ * count.
+ */
+#define W4A16_PLAN_DECODE 0x10u   /* small-M streaming kernel, X held in LDS */
+#define W4A16_PLAN_SPLITK 0x20u   /* split-K streaming kernel (M <= 32) */
+#define W4A16_PLAN_TILED  0x30u   /* LDS-tiled MFMA kernel */
+#define W4A16_PLAN_MASK   0x30u
+#define W4A16_PLAN_PARAM_SHIFT 8
+#define W4A16_PLAN_PARAM(n) (((uint32_t)(n) & 0xFFu) << W4A16_PLAN_PARAM_SHIFT)
+#define W4A16_PLAN_BITS   (W4A16_PLAN_MASK | (0xFFu << W4A16_PLAN_PARAM_SHIFT))
 
 /* W4A16_ABI_VERSION of the loaded library. */
 int w4a16_abi_version(void);
@@ -119,7 +137,10 @@ size_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int group_size, ui
  * dequantized weights exist only in registers.
  *
  *   X          dev, [M][K] row-major, fp16 or bf16 per flags.
- *   packed     dev, blob from w4a16_repack with the same K, N, G and flags.
+ *   packed     dev, blob from w4a16_repack with the same K, N, G and dtype/sym
+ *              flags.
+ *   flags      the blob's W4A16_FP16|BF16 and ASYM|SYM bits, plus optional
+ *              W4A16_PLAN_* hints (the same as given to w4a16_workspace_bytes).
  *   Y          dev, output [M][N] row-major, same dtype as X.  Must not overlap
  *              X, packed or workspace.
  *   workspace  dev, >= w4a16_workspace_bytes(M, N, K, G, flags) bytes (may be
@@ -127,14 +148,15 @@ size_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int group_size, ui
  *              use; every call leaves its counters zero again, so one
  *              zero-fill suffices for any number of calls.  Calls that share a
  *              workspace must not run concurrently.
- * Kernel choice: M <= 32 uses a split-K streaming kernel (every wave streams
- * an equal contiguous share of the weight chunks; partial sums of a split
- * column block are reduced in a fixed order, so results are bitwise
- * reproducible run to run); larger M uses an LDS-tiled MFMA kernel.  Both use
- * v_mfma_f32_32x32x16.  The environment variables
- * W4A16_FORCE_VARIANT=splitk|tiled, W4A16_SPLITK_WGS=<n> (split-K workgroup
- * count) and W4A16_SPLITS=<n> (tiled split count) override the choice
- * (benchmarking only; they also change w4a16_workspace_bytes).
+ * Kernel choice (W4A16_PLAN_* hints override it): M <= 8 whose activations
+ * fit in LDS (M*(2K+16) bytes plus a few KiB, up to 160 KiB) uses the decode
+ * kernel (each workgroup streams whole 32-column tiles over all of K, its
+ * waves splitting K, no workspace); other M <= 32 use a split-K streaming
+ * kernel (every wave streams an equal contiguous share of the weight chunks;
+ * partial sums of a split column block are reduced in a fixed order);
+ * larger M uses an LDS-tiled MFMA kernel.  All reduce in a fixed order, so
+ * results are bitwise reproducible run to run, and all use
+ * v_mfma_f32_32x32x16.
  * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.
  */
 w4a16_status_t w4a16_gemm(const void *X, const void *packed, size_t packed_bytes, void *Y,

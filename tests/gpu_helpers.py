@@ -2,7 +2,6 @@
 (via the Python binding) and compare with the CPU oracle."""
 import os
 import sys
-from contextlib import contextmanager
 
 import numpy as np
 
@@ -26,24 +25,6 @@ def say(msg):
     sys.stdout.flush()
 
 
-@contextmanager
-def env(**kv):
-    old = {k: os.environ.get(k) for k in kv}
-    for k, v in kv.items():
-        if v is None:
-            os.environ.pop(k, None)
-        else:
-            os.environ[k] = str(v)
-    try:
-        yield
-    finally:
-        for k, v in old.items():
-            if v is None:
-                os.environ.pop(k, None)
-            else:
-                os.environ[k] = v
-
-
 def check_shapes(p):
     """Host-side check of the operand shapes the kernels assume, before a launch."""
     assert p.X.shape == (p.M, p.K) and p.X.dtype == np.uint16
@@ -54,7 +35,7 @@ def check_shapes(p):
     else:
         assert p.zeros.shape == (p.K // p.G, p.N) and p.zeros.dtype == np.uint8
         assert int(p.zeros.max()) <= 15
-    assert p.N % 128 == 0 and p.K % p.G == 0 and p.G in (32, 64, 128)
+    assert p.N % 128 == 0 and p.K % 256 == 0 and p.K % p.G == 0 and p.G in (32, 64, 128)
 
 
 class OnDevice:
@@ -68,10 +49,10 @@ class OnDevice:
         self.X, self.qw, self.sc, self.zr = self.w4.to_device(p, device)
         self.packed = self.w4.w4a16_repack(self.qw, self.sc, self.zr, p.K, p.N, p.G, self.flags)
 
-    def gemm(self, X=None, M=None):
+    def gemm(self, X=None, M=None, plan=None):
         import torch
         Xd = self.X if X is None else X
-        Y = self.w4.w4a16_gemm(Xd, self.packed, M=M)
+        Y = self.w4.w4a16_gemm(Xd, self.packed, M=M, plan=plan)
         torch.cuda.synchronize()
         return Y
 

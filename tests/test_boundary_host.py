@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_versions_and_status_strings(lib):
     assert w4.w4a16_abi_version() == 1
-    assert w4.w4a16_layout_version() == 1
+    assert w4.w4a16_layout_version() == 2
     for s in range(5):
         assert isinstance(w4.status_string(s), str) and w4.status_string(s)
     assert w4.status_string(99) == "unknown status"
@@ -52,8 +52,11 @@ def test_versions_and_status_strings(lib):
     (8192, 28672, 128, w4.W4A16_FP16, 8192 * 28672 // 2 + 64 * 28672 * 2 + 64 * 28672 // 2 + 16),
     (8192, 28672, 128, w4.W4A16_BF16 | w4.W4A16_SYM, 8192 * 28672 // 2 + 64 * 28672 * 2 + 16),
     (8192, 28672, 32, w4.W4A16_FP16, 8192 * 28672 // 2 + 256 * 28672 * 2 + 256 * 28672 // 2 + 16),
-    (96, 128, 32, w4.W4A16_FP16, 96 * 128 // 2 + 3 * 128 * 2 + 3 * 128 // 2 + 16),
+    (256, 128, 32, w4.W4A16_FP16, 256 * 128 // 2 + 8 * 128 * 2 + 8 * 128 // 2 + 16),
+    (4352, 128, 64, w4.W4A16_BF16, 4352 * 128 // 2 + 68 * 128 * 2 + 68 * 128 // 2 + 16),
     (4096, 4000, 128, 0, 0),      # N % 128
+    (4224, 4096, 128, 0, 0),      # K % 256
+    (96, 128, 32, 0, 0),          # K % 256
     (4096, 4096, 100, 0, 0),      # G unsupported
     (4100, 4096, 128, 0, 0),      # K % G
     (0, 4096, 128, 0, 0),
@@ -75,6 +78,27 @@ def test_workspace_bytes(lib):
         assert ws == 0 or ws > 65536
 
 
+def test_plan_hints(lib):
+    """Plan hints are accepted where a plan is made (workspace size, GEMM) and
+    nowhere else; the decode kernel needs no workspace; a hint that does not
+    apply to the shape falls back to the default choice."""
+    f = w4.W4A16_FP16
+    assert w4.plan_flags(None) == 0
+    assert w4.plan_flags("decode") == 0x10 and w4.plan_flags(("splitk", 3)) == 0x320
+    for bad in ("fast", ("tiled", 256), ("decode", -1)):
+        with pytest.raises(ValueError):
+            w4.plan_flags(bad)
+    assert w4.w4a16_workspace_bytes(4, 28672, 8192, 128, f | w4.plan_flags("decode")) == 0
+    assert w4.w4a16_workspace_bytes(4, 28672, 8192, 128, f) == 0          # decode by default
+    assert w4.w4a16_workspace_bytes(4, 4096, 8192, 128, f | w4.plan_flags(("tiled", 4))) > 0
+    # decode holds X in LDS: M = 8 rows of K = 16384 do not fit, the hint is ignored
+    assert w4.w4a16_workspace_bytes(8, 4096, 1 << 14, 128, f | w4.plan_flags("decode")) == \
+        w4.w4a16_workspace_bytes(8, 4096, 1 << 14, 128, f)
+    assert w4.w4a16_packed_bytes(4096, 4096, 128, f | 0x10) == 0
+    assert lib.w4a16_repack(FAKE, FAKE, FAKE, 256, 256, 128, 0x10, FAKE, 1 << 30, None) == \
+        w4.W4A16_ERR_INVALID_ARG
+
+
 def gemm(lib, X=FAKE, packed=FAKE, pbytes=1 << 40, Y=FAKE, M=8, N=4096, K=4096, G=128, flags=0,
          ws=FAKE, wsb=1 << 40):
     return lib.w4a16_gemm(X, packed, pbytes, Y, M, N, K, G, flags, ws, wsb, None)
@@ -87,6 +111,9 @@ def gemm(lib, X=FAKE, packed=FAKE, pbytes=1 << 40, Y=FAKE, M=8, N=4096, K=4096, 
     (dict(K=0), w4.W4A16_ERR_INVALID_ARG),
     (dict(N=0), w4.W4A16_ERR_INVALID_ARG),
     (dict(N=4000), w4.W4A16_ERR_UNSUPPORTED),            # N % 128
+    (dict(K=4224), w4.W4A16_ERR_UNSUPPORTED),            # K % 256
+    (dict(flags=0x40), w4.W4A16_ERR_INVALID_ARG),        # neither a blob flag nor a plan hint
+
     (dict(G=256), w4.W4A16_ERR_UNSUPPORTED),
     (dict(G=16), w4.W4A16_ERR_UNSUPPORTED),
     (dict(G=100), w4.W4A16_ERR_INVALID_ARG),             # does not divide K
@@ -98,15 +125,15 @@ def gemm(lib, X=FAKE, packed=FAKE, pbytes=1 << 40, Y=FAKE, M=8, N=4096, K=4096, 
     (dict(Y=FAKE_MIS), w4.W4A16_ERR_INVALID_ARG),
     (dict(packed=FAKE_MIS), w4.W4A16_ERR_INVALID_ARG),
     (dict(pbytes=100), w4.W4A16_ERR_INVALID_ARG),        # blob too small
-    (dict(M=8, K=8192, N=4096, ws=NULL), w4.W4A16_ERR_WORKSPACE),
-    (dict(M=8, K=8192, N=4096, wsb=16), w4.W4A16_ERR_WORKSPACE),
-    (dict(M=8, K=8192, N=4096, ws=FAKE_MIS), w4.W4A16_ERR_WORKSPACE),
+    (dict(M=16, K=8192, N=4096, ws=NULL), w4.W4A16_ERR_WORKSPACE),
+    (dict(M=16, K=8192, N=4096, wsb=16), w4.W4A16_ERR_WORKSPACE),
+    (dict(M=16, K=8192, N=4096, ws=FAKE_MIS), w4.W4A16_ERR_WORKSPACE),
     (dict(M=1 << 31), w4.W4A16_ERR_INVALID_ARG),
 ])
 def test_gemm_rejects_before_any_launch(lib, kw, expect):
     if kw.get("ws", FAKE) is not FAKE or kw.get("wsb", 1) == 16:
         # these need a plan that uses a workspace
-        assert w4.w4a16_workspace_bytes(8, 4096, 8192, 128, 0) > 0
+        assert w4.w4a16_workspace_bytes(16, 4096, 8192, 128, 0) > 0
     assert gemm(lib, **kw) == expect
 
 
@@ -119,6 +146,7 @@ def test_gemm_rejects_before_any_launch(lib, kw, expect):
     ("misaligned_scales", w4.W4A16_ERR_INVALID_ARG),
     ("bad_n", w4.W4A16_ERR_UNSUPPORTED),
     ("bad_k", w4.W4A16_ERR_INVALID_ARG),
+    ("k_not_256", w4.W4A16_ERR_UNSUPPORTED),
 ])
 def test_repack_rejects(lib, fn, case, expect):
     K, N, G = 256, 256, 128
@@ -137,6 +165,8 @@ def test_repack_rejects(lib, fn, case, expect):
         N = 200
     elif case == "bad_k":
         K = 200
+    elif case == "k_not_256":
+        K = 384
     if fn == "repack":
         rc = lib.w4a16_repack(qw, sc, zeros, K, N, G, flags, FAKE, pbytes, None)
     else:

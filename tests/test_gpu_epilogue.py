@@ -1,8 +1,9 @@
 """GPU parity of the fused output epilogue (w4a16_gemm_ex, through the C ABI):
 y = aux_op(act(X.deq * col_scale + bias), aux), against the CPU oracle's
 epilogue on the oracle's product.  Every kernel path that stores Y is covered:
-split-K whole blocks, split-K blocks shared inside a workgroup and between
-workgroups, the tiled kernel with and without a split of K.
+the decode kernel (one workgroup per tile, and one workgroup running many
+items in turn), split-K whole blocks, split-K blocks shared inside a workgroup
+and between workgroups, the tiled kernel with and without a split of K.
 
 Bar: max |Y - Y_ref| / Bo <= 2e-3 (fp16) or 1e-2 (bf16), where Bo carries the
 product's bound B through the epilogue (see the oracle).
@@ -12,7 +13,7 @@ import pytest
 
 import oracle
 import w4a16_synth as synth
-from gpu_helpers import TOL, OnDevice, env, lib, say
+from gpu_helpers import TOL, OnDevice, lib, say
 
 pytestmark = pytest.mark.gpu
 
@@ -26,14 +27,17 @@ def _gpu():
     lib()
 
 
-# (label, M, K, N, G, variant, environment overrides)
+# (label, M, K, N, G, plan hint)
 PATHS = [
-    ("splitk-whole-blocks", 3, 2048, 512, 128, "splitk", {}),
-    ("splitk-shared-blocks", 5, 1024, 256, 64, "splitk", {"W4A16_SPLITK_WGS": 3}),
-    ("splitk-m32", 32, 1024, 384, 32, "splitk", {"W4A16_SPLITK_WGS": 2}),
-    ("tiled-mt2-split", 40, 2048, 512, 128, "tiled", {}),
-    ("tiled-mt4", 150, 512, 1024, 64, "tiled", {"W4A16_SPLITS": 1}),
-    ("tiled-mt4-split", 70, 4096, 256, 128, "tiled", {"W4A16_SPLITS": 4}),
+    ("decode-m1", 1, 2048, 512, 128, "decode"),
+    ("decode-m8-one-wg", 8, 1024, 768, 64, ("decode", 1)),
+    ("decode-m20", 20, 1024, 384, 32, ("decode", 5)),
+    ("splitk-whole-blocks", 3, 2048, 512, 128, "splitk"),
+    ("splitk-shared-blocks", 5, 1024, 256, 64, ("splitk", 3)),
+    ("splitk-m32", 32, 1024, 384, 32, ("splitk", 2)),
+    ("tiled-mt2-split", 40, 2048, 512, 128, "tiled"),
+    ("tiled-mt4", 150, 512, 1024, 64, ("tiled", 1)),
+    ("tiled-mt4-split", 70, 4096, 256, 128, ("tiled", 4)),
 ]
 
 # (label, use col_scale, use bias, aux: None | "add" | "mul" | "inplace", activation)
@@ -56,7 +60,7 @@ def operands(p, seed):
 
 
 def run_case(path, epi, dtype):
-    _, M, K, N, G, variant, extra = path
+    _, M, K, N, G, plan = path
     elabel, use_cs, use_bias, aux_mode, act = epi
     sym = dtype == "bf16"
     p = synth.make_problem(M, K, N, G=G, dtype=dtype, sym=sym, seed=M + K + N)
@@ -69,14 +73,13 @@ def run_case(path, epi, dtype):
     bias_t = torch.from_numpy(bias.view(np.int16)).view(tdt).to(dev) if use_bias else None
     aux_t = torch.from_numpy(aux.view(np.int16)).view(tdt).to(dev) if aux_mode else None
     say(f"epilogue {path[0]} / {elabel} / {dtype}: M={M} K={K} N={N} G={G}")
-    with env(W4A16_FORCE_VARIANT=variant, **extra):
-        if aux_mode == "inplace":
-            Y = aux_t.clone().reshape(M, N)
-            w4.w4a16_gemm_ex(d.X, d.packed, Y=Y, col_scale=cs_t, bias=bias_t, aux=Y,
-                             activation=act, aux_op="add")
-        else:
-            Y = w4.w4a16_gemm_ex(d.X, d.packed, col_scale=cs_t, bias=bias_t, aux=aux_t,
-                                 activation=act, aux_op=aux_mode or "add")
+    if aux_mode == "inplace":
+        Y = aux_t.clone().reshape(M, N)
+        w4.w4a16_gemm_ex(d.X, d.packed, Y=Y, col_scale=cs_t, bias=bias_t, aux=Y,
+                         activation=act, aux_op="add", plan=plan)
+    else:
+        Y = w4.w4a16_gemm_ex(d.X, d.packed, col_scale=cs_t, bias=bias_t, aux=aux_t,
+                             activation=act, aux_op=aux_mode or "add", plan=plan)
     torch.cuda.synchronize()
     Yg = d.y_float(Y)
     Yref, B = oracle.gemm(p.X, p.qweight, p.scales, p.zeros, M, N, K, G, dtype, sym)
@@ -128,7 +131,7 @@ def test_epilogue_rejects_bad_arguments():
 
 
 # Full-size shapes of a decoder FFN block, as the fused-block benchmark runs them:
-# (workload, epilogue) with sampled outputs against the oracle.
+# (workload, epilogue), every output element against the oracle.
 FULL = [
     ("decode_m1_k8192_n28672_fp16_asym_g128_outliers", "silu", None),
     ("decode_m8_k8192_n28672_fp16_asym_g128_outliers", "none", "mul"),
@@ -152,16 +155,11 @@ def test_full_size_epilogue(name, act, aux_op):
     Y = w4.w4a16_gemm_ex(d.X, d.packed, col_scale=cs_t, bias=bias_t, aux=aux_t,
                          activation=act, aux_op=aux_op or "add")
     torch.cuda.synchronize()
-    rng = np.random.default_rng(2)
-    ms = np.concatenate([rng.integers(0, p.M, 256), np.full(16, p.M - 1)])
-    ns = np.concatenate([rng.integers(0, p.N, 256), np.arange(16) + p.N - 16])
-    Yref, B = oracle.gemm_at(p.X, p.qweight, p.scales, p.zeros, p.M, p.N, p.K, p.G, p.dtype,
-                             p.sym, ms, ns)
+    Yref, B = oracle.gemm(p.X, p.qweight, p.scales, p.zeros, p.M, p.N, p.K, p.G, p.dtype, p.sym)
     Yo, Bo = oracle.epilogue(Yref, B, p.M, p.N, p.dtype, col_scale=cs, bias=bias,
                              aux=aux if aux_op else None, activation=act,
-                             aux_op=aux_op or "add", ms=ms, ns=ns)
-    Yg = d.y_float(Y)[ms, ns]
-    rel, zero_ok = oracle.max_rel_error(Yg, Yo, Bo)
+                             aux_op=aux_op or "add")
+    rel, zero_ok = oracle.max_rel_error(d.y_float(Y), Yo, Bo)
     assert zero_ok and rel <= TOL[p.dtype], f"{name}: max|Y-Yref|/Bo = {rel:.3e}"
 
 
@@ -172,7 +170,7 @@ def test_neutral_epilogue_is_bitwise_the_plain_product(path, dtype):
     (t = v*1 + 0, identity) and must store exactly what the plain kernels
     store (up to the sign of zero)."""
     from gpu_helpers import same_bits
-    _, M, K, N, G, variant, extra = path
+    _, M, K, N, G, plan = path
     sym = dtype == "bf16"
     p = synth.make_problem(M, K, N, G=G, dtype=dtype, sym=sym, seed=7 * M + N)
     d = OnDevice(p)
@@ -180,8 +178,78 @@ def test_neutral_epilogue_is_bitwise_the_plain_product(path, dtype):
     ones = torch.ones(N, dtype=torch.float32, device=d.X.device)
     zeros = torch.zeros(N, dtype=w4.torch_dtype(d.flags), device=d.X.device)
     say(f"neutral epilogue {path[0]} / {dtype}")
-    with env(W4A16_FORCE_VARIANT=variant, **extra):
-        Y0 = w4.w4a16_gemm(d.X, d.packed)
-        Y1 = w4.w4a16_gemm_ex(d.X, d.packed, col_scale=ones, bias=zeros)
+    Y0 = w4.w4a16_gemm(d.X, d.packed, plan=plan)
+    Y1 = w4.w4a16_gemm_ex(d.X, d.packed, col_scale=ones, bias=zeros, plan=plan)
     torch.cuda.synchronize()
     assert same_bits(w4.bits_of(Y0), w4.bits_of(Y1))
+
+
+def _bits(t):
+    return t.cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("M,Hd,F", [(1, 8192, 28672), (8, 1024, 2048), (40, 1024, 2048)])
+def test_ffn_chain_matches_oracle(M, Hd, F):
+    """A decoder FFN block as three fused calls, Gt = silu(X Wg),
+    Ht = (X Wu) * Gt, Y = Ht Wd + X (fp16, G = 128).
+
+    Each call is compared with the oracle fed the same operands the GPU call
+    read (the GPU's own Gt and Ht), every output element, to the product's bar
+    tol * Bo.  The chain's end is then compared with the oracle chain (the
+    oracle's own intermediates, rounded to fp16 as the library stores them).
+    First-order propagation bounds their difference: |Gt - G_or| <= 2 tol Bo1
+    (the call's error plus the oracle's rounding), so
+    |Ht - H_or| <= tol (Bo2 + Bo2_or + 2 Bu Bo1) =: tol D with Bu the bound of
+    X Wu, and |Y - Y_or| <= tol (Bo3 + sum_k D[m][k] |Wd[k][n]|)."""
+    w4 = lib()
+    G, dt = 128, "fp16"
+    tol = TOL[dt]
+    flags = w4.flags_of(dt, False)
+    dev = torch.device("cuda")
+    say(f"ffn chain M={M} H={Hd} F={F}")
+    probs = [synth.make_problem(1, K, N, G=G, dtype=dt, sym=False, seed=seed)
+             for seed, (K, N) in ((31, (Hd, F)), (32, (Hd, F)), (33, (F, Hd)))]
+    blobs = []
+    for p in probs:
+        _, qw, sc, zr = w4.to_device(p, dev)
+        blobs.append(w4.w4a16_repack(qw, sc, zr, p.K, p.N, G, flags))
+    Xb = synth.make_activations(M, Hd, dt, seed=9)
+    X = torch.from_numpy(Xb.view(np.int16)).view(torch.float16).to(dev)
+    Gt = w4.w4a16_gemm_ex(X, blobs[0], activation="silu")
+    Ht = w4.w4a16_gemm_ex(X, blobs[1], aux=Gt, aux_op="mul")
+    Y = w4.w4a16_gemm_ex(Ht, blobs[2], aux=X, aux_op="add")
+    torch.cuda.synchronize()
+    Gb, Hb, Yb = _bits(Gt), _bits(Ht), _bits(Y)
+    pg, pu, pd = probs
+
+    def product(p, Xin):
+        return oracle.gemm(Xin, p.qweight, p.scales, p.zeros, M, p.N, p.K, G, dt, False)
+
+    def f(b):
+        return oracle.bits_to_float(b, dt)
+
+    yg, bg = product(pg, Xb)
+    yu, bu = product(pu, Xb)
+    g_ref, g_bo = oracle.epilogue(yg, bg, M, F, dt, activation="silu")
+    h_ref, h_bo = oracle.epilogue(yu, bu, M, F, dt, aux=Gb, aux_op="mul")
+    yd, bd = product(pd, Hb)
+    y_ref, y_bo = oracle.epilogue(yd, bd, M, Hd, dt, aux=Xb, aux_op="add")
+    # stage by stage, on the GPU's own operands
+    for name, got, ref, bo in (("gate", Gb, g_ref, g_bo), ("up*gate", Hb, h_ref, h_bo),
+                               ("down+res", Yb, y_ref, y_bo)):
+        rel, zero_ok = oracle.max_rel_error(f(got), ref, bo)
+        assert zero_ok and rel <= tol, f"{name}: max|Y-Yref|/Bo = {rel:.3e}"
+    # the oracle's own chain
+    g_or = synth.to_dtype_bits(g_ref, dt)
+    h_or, h_or_bo = oracle.epilogue(yu, bu, M, F, dt, aux=g_or, aux_op="mul")
+    yo, bo = product(pd, synth.to_dtype_bits(h_or, dt))
+    y_or, y_or_bo = oracle.epilogue(yo, bo, M, Hd, dt, aux=Xb, aux_op="add")
+    # sum_k D[m][k] |Wd[k][n]| is the bound column of a product whose
+    # activations are D (rounded up to fp16, scaled by a power of two to fit)
+    D = (h_bo + h_or_bo + 2.0 * bu * g_bo) * (1 + 2.0 ** -9)
+    sc = 2.0 ** max(0, int(np.ceil(np.log2(max(float(D.max()), 1.0) / 16384.0))))
+    _, carried = product(pd, synth.to_dtype_bits(D / sc, dt))
+    bound = tol * (np.maximum(y_bo, y_or_bo) + sc * carried)
+    err = np.abs(f(Yb) - y_or)
+    worst = float(np.max(err / np.where(bound > 0, bound, np.inf)))
+    assert np.all(err <= bound), f"chain end: max err/bound = {worst:.3f}"

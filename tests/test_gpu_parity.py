@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 import w4a16_synth as synth
-from gpu_helpers import (OnDevice, assert_gemm_close, column_slice, env, lib, same_bits, say)
+from gpu_helpers import (OnDevice, assert_gemm_close, column_slice, lib, same_bits, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -58,8 +58,8 @@ def test_mfma_operand_layout(dtype):
 SHAPES = [  # (K, N, G, dtype, sym)
     (256, 128, 128, "fp16", False),
     (512, 384, 64, "bf16", False),
-    (96, 256, 32, "fp16", True),
-    (160, 640, 32, "bf16", True),
+    (256, 256, 32, "fp16", True),
+    (768, 640, 32, "bf16", True),
     (1024, 512, 128, "bf16", False),
 ]
 
@@ -99,7 +99,8 @@ def test_dequant_exhaustive_scales(dtype):
     G, N = 32, 4096
     scales_all = np.arange(0, 0x7C00 if dtype == "fp16" else 0x7F80, dtype=np.uint16)
     combos = 16 * scales_all.size                      # (z, s) pairs
-    NG = -(-combos // N)
+    per_body = 256 // G                                # K must be a multiple of 256
+    NG = -(-combos // (N * per_body)) * per_body
     K = NG * G
     zs = np.repeat(np.arange(16, dtype=np.uint8), scales_all.size)
     ss = np.tile(scales_all, 16)
@@ -139,25 +140,25 @@ def one_hot_rows(M, K, dtype):
     return X, ks
 
 
-@pytest.mark.parametrize("variant,M", [("splitk", 1), ("splitk", 7), ("splitk", 32),
+@pytest.mark.parametrize("variant,M", [("decode", 1), ("decode", 8), ("decode", 32),
+                                       ("splitk", 1), ("splitk", 7), ("splitk", 32),
                                        ("tiled", 20), ("tiled", 64), ("tiled", 130)])
 @pytest.mark.parametrize("K,N,G,dtype,sym", [(512, 384, 128, "fp16", False),
                                              (256, 256, 32, "bf16", False),
-                                             (384, 640, 64, "fp16", True)])
+                                             (768, 640, 64, "fp16", True)])
 def test_gemm_one_hot_rows_are_dequantized_weights(variant, M, K, N, G, dtype, sym):
     """X = rows of the identity: Y[m] must equal deq[k_m] bit for bit, through the
     real GEMM kernels (one exact product, fp32 sums of zeros)."""
     p = synth.make_problem(M, K, N, G=G, dtype=dtype, sym=sym, seed=M + K)
     p.X, ks = one_hot_rows(M, K, dtype)
     say(f"one-hot {variant} M={M} K={K} N={N} G={G} {dtype} sym={sym}")
-    with env(W4A16_FORCE_VARIANT=variant):
-        d = OnDevice(p)
-        Y = d.w4.bits_of(d.gemm())
+    d = OnDevice(p)
+    Y = d.w4.bits_of(d.gemm(plan=variant))
     deq = oracle.dequant(p.qweight, p.scales, p.zeros, K, N, G, dtype, sym)
     assert same_bits(Y, deq[ks])
 
 
-@pytest.mark.parametrize("variant,M", [("splitk", 3), ("tiled", 70)])
+@pytest.mark.parametrize("variant,M", [("decode", 3), ("splitk", 3), ("tiled", 70)])
 def test_gemm_exact_bf16_form_for_huge_scales(variant, M):
     """bf16 scales so large that -z*s overflows fp32 (z = 15, s near 2^125) while
     every (q - z) * s stays finite (q in {14, 15}): the repack flags the blob and
@@ -171,11 +172,10 @@ def test_gemm_exact_bf16_form_for_huge_scales(variant, M):
     X, ks = one_hot_rows(M, K, "bf16")
     p = synth.Problem(M, K, N, G, "bf16", False, X, synth.pack_nibbles(q), scales, zeros)
     say(f"exact bf16 form {variant} M={M}")
-    with env(W4A16_FORCE_VARIANT=variant):
-        d = OnDevice(p)
-        flags_word = int(d.packed.data[-8:-4].view(torch.int32).cpu()[0])
-        assert flags_word & 1, "repack did not flag the blob"
-        Y = w4.bits_of(d.gemm())
+    d = OnDevice(p)
+    flags_word = int(d.packed.data[-8:-4].view(torch.int32).cpu()[0])
+    assert flags_word & 1, "repack did not flag the blob"
+    Y = w4.bits_of(d.gemm(plan=variant))
     deq = oracle.dequant(p.qweight, p.scales, p.zeros, K, N, G, "bf16", False)
     assert same_bits(Y, deq[ks])
     assert same_bits(w4.bits_of(w4.w4a16_dequant(d.packed)), deq)
@@ -183,9 +183,9 @@ def test_gemm_exact_bf16_form_for_huge_scales(variant, M):
 
 SMALL = [  # (K, N, G, dtype, sym)
     (256, 256, 128, "fp16", False),
-    (96, 384, 32, "bf16", True),
-    (640, 128, 64, "bf16", False),
-    (160, 512, 32, "fp16", False),
+    (512, 384, 32, "bf16", True),
+    (768, 128, 64, "bf16", False),
+    (1280, 512, 32, "fp16", False),
     (2048, 640, 128, "fp16", True),
 ]
 
@@ -201,22 +201,25 @@ def test_gemm_matches_oracle(M, K, N, G, dtype, sym):
     assert_gemm_close(p, Yg, Yref, B, f"M={M}")
 
 
-@pytest.mark.parametrize("variant,M,splits", [("splitk", 4, 1), ("splitk", 4, 3), ("splitk", 30, 16),
-                                              ("splitk", 1, 7), ("splitk", 9, 100), ("splitk", 2, 5000),
-                                              ("tiled", 8, 1), ("tiled", 32, 2), ("tiled", 96, 5),
-                                              ("tiled", 200, 16)])
-def test_gemm_forced_variant_and_splits(variant, M, splits):
-    """Forced kernel and work split: for split-K, `splits` is the number of
-    workgroups (1 = one workgroup streams everything; 5000 = more than chunks)."""
+@pytest.mark.parametrize("variant,M,param", [("decode", 1, 1), ("decode", 5, 3), ("decode", 8, 7),
+                                             ("decode", 20, 2), ("decode", 32, 255),
+                                             ("splitk", 4, 1), ("splitk", 4, 3), ("splitk", 30, 16),
+                                             ("splitk", 1, 7), ("splitk", 9, 100), ("splitk", 2, 255),
+                                             ("tiled", 8, 1), ("tiled", 32, 2), ("tiled", 96, 5),
+                                             ("tiled", 200, 16)])
+def test_gemm_forced_variant_and_param(variant, M, param):
+    """Forced kernel and work split.  decode: `param` workgroups share the 20
+    output tiles (1 = one workgroup runs every item in turn, so the item slots
+    are reused many times); split-K: 8*param workgroups (2040 = more than
+    there are batches); tiled: `param` K-splits."""
     K, N, G = 4096, 640, 64
     p = synth.make_problem(M, K, N, G=G, dtype="bf16", sym=False, seed=M)
-    say(f"forced {variant} S={splits} M={M}")
-    with env(W4A16_FORCE_VARIANT=variant, W4A16_SPLITS=splits, W4A16_SPLITK_WGS=splits):
-        d = OnDevice(p)
-        Y1 = d.gemm()
-        Y2 = d.gemm()
+    say(f"forced {variant} param={param} M={M}")
+    d = OnDevice(p)
+    Y1 = d.gemm(plan=(variant, param))
+    Y2 = d.gemm(plan=(variant, param))
     Yref, B = oracle.gemm(p.X, p.qweight, p.scales, p.zeros, M, N, K, G, "bf16", False)
-    assert_gemm_close(p, d.y_float(Y1), Yref, B, f"{variant} S={splits}")
+    assert_gemm_close(p, d.y_float(Y1), Yref, B, f"{variant} param={param}")
     assert torch.equal(Y1.view(torch.int16), Y2.view(torch.int16)), "not bitwise reproducible"
 
 
@@ -230,15 +233,16 @@ def test_workspace_counters_return_to_zero():
     for i, (M, K, N, var) in enumerate([(1, 8192, 1024, "splitk"), (9, 2048, 512, "splitk"),
                                         (40, 4096, 1024, "tiled"), (3, 8192, 1024, "splitk"),
                                         (70, 8192, 384, "tiled"), (2, 8192, 4096, "splitk"),
-                                        (1, 4096, 256, "splitk"), (5, 8192, 8192, "splitk")]):
+                                        (1, 4096, 256, "splitk"), (5, 8192, 8192, "splitk"),
+                                        (1, 4096, 1024, "decode"), (8, 8192, 4096, "decode"),
+                                        (4, 2048, 512, "splitk")]):
         p = synth.make_problem(M, K, N, G=128, seed=i)
         say(f"workspace reuse call {i}: M={M} K={K} N={N} {var}")
-        with env(W4A16_FORCE_VARIANT=var):
-            need = w4.w4a16_workspace_bytes(M, N, K, 128, 0)
-            assert need > 0
-            d = OnDevice(p)
-            Y = w4.w4a16_gemm(d.X, d.packed, workspace=ws)
-            torch.cuda.synchronize()
+        need = w4.w4a16_workspace_bytes(M, N, K, 128, w4.plan_flags(var))
+        assert (need == 0) == (var == "decode")      # the decode kernel needs none
+        d = OnDevice(p)
+        Y = w4.w4a16_gemm(d.X, d.packed, workspace=ws, plan=var)
+        torch.cuda.synchronize()
         Yref, B = oracle.gemm(p.X, p.qweight, p.scales, p.zeros, M, N, K, 128, "fp16", False)
         assert_gemm_close(p, d.y_float(Y), Yref, B, f"call {i}")
         # counter area: the first 64 KiB of every workspace, all zero between calls
@@ -266,22 +270,28 @@ def full_problem(name):
 
 @pytest.mark.parametrize("name", list(synth.WORKLOADS))
 def test_full_size_workload(name):
-    """Launch configuration of the benchmark at the workload's real size; sampled
-    outputs against the oracle, and one 128-column slice of the dequantized
-    weights bit-exact."""
+    """Launch configuration of the benchmark at the workload's real size.  Up to
+    M = 128 every output element is compared with the oracle; above, rows are
+    sampled (the prefill test below covers those shapes densely).  One
+    128-column slice of the dequantized weights is compared bit for bit."""
     w4 = lib()
     p = full_problem(name)
     say(f"full-size {name}: M={p.M} K={p.K} N={p.N} G={p.G} {p.dtype} sym={p.sym}")
     d = OnDevice(p)
     Y = d.gemm()
     rng = np.random.default_rng(1)
-    n_s = 384
-    ms = np.concatenate([rng.integers(0, p.M, n_s), np.full(32, p.M - 1), np.zeros(32, int)])
-    ns = np.concatenate([rng.integers(0, p.N, n_s), rng.integers(0, p.N, 32), np.arange(32) + p.N - 32])
-    Yref, B = oracle.gemm_at(p.X, p.qweight, p.scales, p.zeros, p.M, p.N, p.K, p.G, p.dtype, p.sym,
-                             ms, ns)
-    Yg = d.y_float(Y)[ms, ns]
-    assert_gemm_close(p, Yg, Yref, B, name)
+    if p.M <= 128:
+        Yref, B = oracle.gemm(p.X, p.qweight, p.scales, p.zeros, p.M, p.N, p.K, p.G, p.dtype,
+                              p.sym)
+        assert_gemm_close(p, d.y_float(Y), Yref, B, name)
+    else:
+        n_s = 384
+        ms = np.concatenate([rng.integers(0, p.M, n_s), np.full(32, p.M - 1), np.zeros(32, int)])
+        ns = np.concatenate([rng.integers(0, p.N, n_s), rng.integers(0, p.N, 32),
+                             np.arange(32) + p.N - 32])
+        Yref, B = oracle.gemm_at(p.X, p.qweight, p.scales, p.zeros, p.M, p.N, p.K, p.G, p.dtype,
+                                 p.sym, ms, ns)
+        assert_gemm_close(p, d.y_float(Y)[ms, ns], Yref, B, name)
     # dequant: one column block, bit-exact
     nb = int(rng.integers(0, p.N // 128))
     cols = np.arange(nb * 128, nb * 128 + 128)
@@ -315,19 +325,25 @@ PREFILL = [n for n in synth.WORKLOADS if n.startswith("prefill_")]
 
 @pytest.mark.parametrize("name", PREFILL)
 def test_prefill_dense_samples(name):
-    """Prefill at full size in the benchmark's launch configuration: 8 random
-    rows over every output column and every row over 32 random columns,
-    against the oracle element by element."""
+    """Prefill at full size in the benchmark's launch configuration, against the
+    oracle element by element: 64 random rows over every output column, and
+    every row over 256 columns (the first 64, the last 64 and 128 random
+    ones)."""
     p = full_problem(name)
     say(f"prefill dense samples {name}: M={p.M} K={p.K} N={p.N}")
     d = OnDevice(p)
     Y = d.gemm()
-    Yf = d.y_float(Y)
+    Yb = d.w4.bits_of(Y)
+    del Y
     rng = np.random.default_rng(7)
-    rows = rng.choice(p.M, 8, replace=False)
-    cols = rng.choice(p.N, 32, replace=False)
-    ms = np.concatenate([np.repeat(rows, p.N), np.tile(np.arange(p.M), 32)])
-    ns = np.concatenate([np.tile(np.arange(p.N), 8), np.repeat(cols, p.M)])
-    Yref, B = oracle.gemm_at(p.X, p.qweight, p.scales, p.zeros, p.M, p.N, p.K, p.G, p.dtype,
-                             p.sym, ms, ns)
-    assert_gemm_close(p, Yf[ms, ns], Yref, B, name)
+    rows = np.sort(rng.choice(p.M, 64, replace=False))
+    Xr = np.ascontiguousarray(p.X[rows])
+    Yref, B = oracle.gemm(Xr, p.qweight, p.scales, p.zeros, 64, p.N, p.K, p.G, p.dtype, p.sym)
+    sub = synth.Problem(64, p.K, p.N, p.G, p.dtype, p.sym, Xr, p.qweight, p.scales, p.zeros)
+    assert_gemm_close(sub, oracle.bits_to_float(Yb[rows], p.dtype), Yref, B, f"{name} rows")
+    inner = rng.choice(np.arange(64, p.N - 64), 128, replace=False)
+    cols = np.sort(np.concatenate([np.arange(64), np.arange(p.N - 64, p.N), inner]))
+    sl = column_slice(p, cols)
+    Yref, B = oracle.gemm(sl.X, sl.qweight, sl.scales, sl.zeros, p.M, sl.N, p.K, p.G, p.dtype,
+                          p.sym)
+    assert_gemm_close(sl, oracle.bits_to_float(Yb[:, cols], p.dtype), Yref, B, f"{name} cols")

@@ -102,6 +102,24 @@ def test_bias_and_aux_decode_their_dtype(oracle_mod):
     assert list(Yo[0]) == [0.333984375, -2.0]
 
 
+def test_silu_slope_stays_below_the_bound_constant(oracle_mod):
+    """The error bound carries a perturbation of t through SiLU with L = 1.1.
+    SiLU's slope sigma(t) (1 + t (1 - sigma(t))) peaks near t = 2.3994 at about
+    1.0998 and dips to about -0.0998 near t = -2.3994, so |silu'| < 1.1: every
+    difference quotient of the oracle's SiLU over a dense grid stays inside
+    (-1.1, 1.1), and the extremes come within 1e-3 of those values (a looser
+    L would hide nothing, a SiLU with the wrong slope fails)."""
+    t = np.linspace(-30.0, 30.0, 600001)
+    Yo, _ = oracle_mod.epilogue(t[None, :], np.abs(t)[None, :], 1, t.size, "fp16",
+                                activation="silu")
+    q = np.diff(Yo[0]) / np.diff(t)
+    assert q.max() < 1.1 and q.min() > -1.1
+    assert abs(q.max() - 1.0998) < 1e-3 and abs(q.min() + 0.0998) < 1e-3
+    assert abs(t[np.argmax(q)] - 2.3994) < 1e-2
+    # far from 0 the slope tends to 1 on the right and 0 on the left
+    assert abs(q[-1] - 1.0) < 1e-9 and abs(q[0]) < 1e-9
+
+
 @pytest.mark.parametrize("act", ["none", "relu", "silu"])
 @pytest.mark.parametrize("aux_op", ["add", "mul"])
 def test_bound_covers_the_output(oracle_mod, act, aux_op):

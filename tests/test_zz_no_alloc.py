@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 import w4a16_synth as synth
-from gpu_helpers import TOL, OnDevice, env, lib, say
+from gpu_helpers import TOL, OnDevice, lib, say
 
 pytestmark = pytest.mark.gpu
 
@@ -23,35 +23,34 @@ def _gpu():
     lib()
 
 
-# (label, M, K, N, G, dtype, sym, variant, overrides): each needs scratch, the
-# second of each pair is smaller than the first
+# (label, M, K, N, G, dtype, sym, plan hint): each needs scratch, the second of
+# each pair is smaller than the first
 PAIRS = [
-    (("tiled-split", 70, 4096, 1024, 128, "fp16", False, "tiled", {"W4A16_SPLITS": 4}),
-     ("splitk-shared", 5, 2048, 512, 64, "fp16", False, "splitk", {"W4A16_SPLITK_WGS": 3})),
-    (("splitk-shared", 9, 8192, 4096, 128, "bf16", True, "splitk", {}),
-     ("tiled-split", 40, 1024, 256, 32, "bf16", True, "tiled", {"W4A16_SPLITS": 2})),
+    (("tiled-split", 70, 4096, 1024, 128, "fp16", False, ("tiled", 4)),
+     ("splitk-shared", 5, 2048, 512, 64, "fp16", False, ("splitk", 3))),
+    (("splitk-shared", 9, 8192, 4096, 128, "bf16", True, "splitk"),
+     ("tiled-split", 40, 1024, 256, 32, "bf16", True, ("tiled", 2))),
 ]
 
 
 def run_pair(pair, with_epilogue):
     w4 = lib()
-    for label, M, K, N, G, dtype, sym, variant, extra in pair:
+    for label, M, K, N, G, dtype, sym, plan in pair:
         p = synth.make_problem(M, K, N, G=G, dtype=dtype, sym=sym, seed=M * 7 + N)
         say(f"noalloc {label}: M={M} K={K} N={N} G={G} {dtype} sym={sym} ep={with_epilogue}")
-        with env(W4A16_FORCE_VARIANT=variant, **extra):
-            need = w4.w4a16_workspace_bytes(M, N, K, G, w4.flags_of(dtype, sym))
-            assert 0 < need <= w4.W4A16_NOALLOC_SCRATCH_BYTES, (label, need)
-            d = OnDevice(p)
-            kw = {}
-            if with_epilogue:
-                rng = np.random.default_rng(N)
-                kw = dict(col_scale=torch.from_numpy(rng.uniform(-1, 1, N).astype(np.float32)).cuda(),
-                          bias=torch.from_numpy(rng.normal(0, 0.5, N)).to(d.X.dtype).cuda(),
-                          activation="silu")
-            Y_ref = d.w4.w4a16_gemm_ex(d.X, d.packed, **kw)
-            Y = torch.full((M, N), float("nan"), dtype=d.X.dtype, device=d.X.device)
-            w4.w4a16_gemm_noalloc(d.X, d.packed, Y, **kw)
-            torch.cuda.synchronize()
+        need = w4.w4a16_workspace_bytes(M, N, K, G, w4.flags_of(dtype, sym) | w4.plan_flags(plan))
+        assert 0 < need <= w4.W4A16_NOALLOC_SCRATCH_BYTES, (label, need)
+        d = OnDevice(p)
+        kw = dict(plan=plan)
+        if with_epilogue:
+            rng = np.random.default_rng(N)
+            kw.update(col_scale=torch.from_numpy(rng.uniform(-1, 1, N).astype(np.float32)).cuda(),
+                      bias=torch.from_numpy(rng.normal(0, 0.5, N)).to(d.X.dtype).cuda(),
+                      activation="silu")
+        Y_ref = d.w4.w4a16_gemm_ex(d.X, d.packed, **kw)
+        Y = torch.full((M, N), float("nan"), dtype=d.X.dtype, device=d.X.device)
+        w4.w4a16_gemm_noalloc(d.X, d.packed, Y, **kw)
+        torch.cuda.synchronize()
         assert torch.equal(Y.view(torch.int16), Y_ref.view(torch.int16)), label
         if not with_epilogue:
             Yref, B = oracle.gemm(p.X, p.qweight, p.scales, p.zeros, M, N, K, G, dtype, sym)

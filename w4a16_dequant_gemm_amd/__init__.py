@@ -29,6 +29,21 @@ W4A16_FP16 = 0x0
 W4A16_BF16 = 0x1
 W4A16_ASYM = 0x0
 W4A16_SYM = 0x2
+# plan hints (flags of w4a16_workspace_bytes and the GEMM calls only)
+W4A16_PLAN = {"decode": 0x10, "splitk": 0x20, "tiled": 0x30}
+W4A16_PLAN_PARAM_SHIFT = 8
+
+
+def plan_flags(plan) -> int:
+    """Flag bits of a plan hint: None, a variant name ("decode", "splitk",
+    "tiled") or (name, parameter) -- tiles per decode item, split-K workgroups
+    in units of 8, or the tiled kernel's split count."""
+    if plan is None:
+        return 0
+    name, param = (plan, 0) if isinstance(plan, str) else plan
+    if name not in W4A16_PLAN or not 0 <= int(param) <= 255:
+        raise ValueError(f"bad plan hint {plan!r}")
+    return W4A16_PLAN[name] | (int(param) << W4A16_PLAN_PARAM_SHIFT)
 
 # entry points declared in include/w4a16.h
 C_FUNCTIONS = (
@@ -177,9 +192,8 @@ def w4a16_workspace_bytes(M: int, N: int, K: int, group_size: int, flags: int) -
 
 
 def _workspace_need(M, N, K, G, flags) -> int:
-    # the plan depends on the shape and on the W4A16_* environment overrides
-    key = (M, N, K, G, flags, os.environ.get("W4A16_FORCE_VARIANT"),
-           os.environ.get("W4A16_SPLITK_WGS"), os.environ.get("W4A16_SPLITS"))
+    # the plan depends on the shape and the flags (plan hints included) only
+    key = (M, N, K, G, flags)
     need = _ws_bytes.get(key)
     if need is None:
         need = _ws_bytes[key] = w4a16_workspace_bytes(M, N, K, G, flags)
@@ -203,8 +217,8 @@ def w4a16_repack(qweight: torch.Tensor, scales: torch.Tensor, zeros: Optional[to
     flags) and zeros uint8 [K/G][N] (None for the symmetric format) -> PackedW4."""
     nbytes = w4a16_packed_bytes(K, N, group_size, flags)
     if nbytes == 0:
-        raise W4A16Error(W4A16_ERR_UNSUPPORTED if N % 128 else W4A16_ERR_INVALID_ARG,
-                         "w4a16_packed_bytes")
+        raise W4A16Error(W4A16_ERR_UNSUPPORTED if (N % 128 or K % 256) else
+                         W4A16_ERR_INVALID_ARG, "w4a16_packed_bytes")
     dev = qweight.device
     if qweight.dtype not in (torch.int32, torch.uint32) or qweight.numel() != (K // 8) * N \
             or not qweight.is_contiguous() or not qweight.is_cuda:
@@ -300,11 +314,13 @@ def _gemm_args(where, X, packed, M, Y, col_scale=None, bias=None, aux=None, acti
 
 def w4a16_gemm(X: torch.Tensor, packed: PackedW4, M: Optional[int] = None,
                Y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-               stream=None) -> torch.Tensor:
-    """Y[M][N] = X[M][K] . dequant(packed); X is [M][K] fp16/bf16 on the device."""
+               stream=None, plan=None) -> torch.Tensor:
+    """Y[M][N] = X[M][K] . dequant(packed); X is [M][K] fp16/bf16 on the device.
+    `plan`: an optional kernel hint (see plan_flags)."""
     lib = load_library()
     M, Y, _ = _gemm_args("w4a16_gemm", X, packed, M, Y)
-    K, N, G, flags = packed.K, packed.N, packed.group_size, packed.flags
+    K, N, G = packed.K, packed.N, packed.group_size
+    flags = packed.flags | plan_flags(plan)
     if workspace is None:
         workspace = workspace_for(_workspace_need(M, N, K, G, flags), X.device, stream)
     _check(lib.w4a16_gemm(_ptr(X), _ptr(packed.data), packed.data.numel(), _ptr(Y), M, N, K, G,
@@ -317,14 +333,15 @@ def w4a16_gemm_ex(X: torch.Tensor, packed: PackedW4, M: Optional[int] = None,
                   Y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                   stream=None, *, col_scale: Optional[torch.Tensor] = None,
                   bias: Optional[torch.Tensor] = None, aux: Optional[torch.Tensor] = None,
-                  activation: str = "none", aux_op: str = "add") -> torch.Tensor:
+                  activation: str = "none", aux_op: str = "add", plan=None) -> torch.Tensor:
     """w4a16_gemm with the fused output epilogue
     Y = aux_op(act(X.deq * col_scale + bias), aux): col_scale fp32 [N], bias [N]
     and aux [M][N] in X's dtype, each optional (device tensors)."""
     lib = load_library()
     M, Y, ep = _gemm_args("w4a16_gemm_ex", X, packed, M, Y, col_scale, bias, aux, activation,
                           aux_op)
-    K, N, G, flags = packed.K, packed.N, packed.group_size, packed.flags
+    K, N, G = packed.K, packed.N, packed.group_size
+    flags = packed.flags | plan_flags(plan)
     if workspace is None:
         workspace = workspace_for(_workspace_need(M, N, K, G, flags), X.device, stream)
     _check(lib.w4a16_gemm_ex(_ptr(X), _ptr(packed.data), packed.data.numel(), _ptr(Y), M, N, K,
@@ -338,7 +355,7 @@ def w4a16_gemm_noalloc(X: torch.Tensor, packed: PackedW4, Y: torch.Tensor,
                        M: Optional[int] = None, stream=None, *,
                        col_scale: Optional[torch.Tensor] = None,
                        bias: Optional[torch.Tensor] = None, aux: Optional[torch.Tensor] = None,
-                       activation: str = "none", aux_op: str = "add") -> torch.Tensor:
+                       activation: str = "none", aux_op: str = "add", plan=None) -> torch.Tensor:
     """w4a16_gemm_ex without a workspace: the library's static per-GPU scratch
     (W4A16_NOALLOC_SCRATCH_BYTES) serves instead, and nothing is allocated.
     The caller provides Y.  Calls that may overlap in time on one GPU race."""
@@ -348,7 +365,8 @@ def w4a16_gemm_noalloc(X: torch.Tensor, packed: PackedW4, Y: torch.Tensor,
     M, Y, ep = _gemm_args("w4a16_gemm_noalloc", X, packed, M, Y, col_scale, bias, aux,
                           activation, aux_op)
     _check(lib.w4a16_gemm_noalloc(_ptr(X), _ptr(packed.data), packed.data.numel(), _ptr(Y), M,
-                                  packed.N, packed.K, packed.group_size, packed.flags,
+                                  packed.N, packed.K, packed.group_size,
+                                  packed.flags | plan_flags(plan),
                                   None if ep is None else ctypes.byref(ep), _stream(stream)),
            "w4a16_gemm_noalloc")
     return Y

@@ -10,7 +10,7 @@ import tempfile
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libw4a16.so")
-HEADERS = ["w4a16_layout.h", "w4a16_device.h", "w4a16_internal.h"]
+HEADERS = ["w4a16_layout.h", "w4a16_device.h", "w4a16_internal.h", "w4a16_epilogue.h"]
 
 COMMON = [
     "--offload-arch=gfx950",
@@ -22,8 +22,9 @@ COMMON = [
     "-Wall",
 ]
 
-# (source, extra defines): w4a16_gemm.hip is compiled once per (activation
-# dtype, epilogue) pair so that its kernel instantiations compile in parallel.
+# (source, extra defines): w4a16_gemm.hip and w4a16_decode.hip are compiled
+# once per (activation dtype, epilogue) pair so that their kernel
+# instantiations compile in parallel.
 UNITS = [
     ("w4a16_api.cpp", []),
     ("w4a16_repack.hip", []),
@@ -32,6 +33,10 @@ UNITS = [
     ("w4a16_gemm.hip", ["-DW4A16_TU_BF16=1", "-DW4A16_TU_EP=0"]),
     ("w4a16_gemm.hip", ["-DW4A16_TU_BF16=0", "-DW4A16_TU_EP=1"]),
     ("w4a16_gemm.hip", ["-DW4A16_TU_BF16=1", "-DW4A16_TU_EP=1"]),
+    ("w4a16_decode.hip", ["-DW4A16_TU_BF16=0", "-DW4A16_TU_EP=0"]),
+    ("w4a16_decode.hip", ["-DW4A16_TU_BF16=1", "-DW4A16_TU_EP=0"]),
+    ("w4a16_decode.hip", ["-DW4A16_TU_BF16=0", "-DW4A16_TU_EP=1"]),
+    ("w4a16_decode.hip", ["-DW4A16_TU_BF16=1", "-DW4A16_TU_EP=1"]),
 ]
 
 

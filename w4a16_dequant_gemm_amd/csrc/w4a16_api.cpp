@@ -6,6 +6,9 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
+#include <atomic>
+
 #include "../../include/w4a16.h"
 #include "w4a16_internal.h"
 
@@ -13,7 +16,8 @@ namespace w4a16 {
 
 namespace {
 
-constexpr int kNumCUs = 256;        // MI355X compute units
+constexpr int kDefaultCUs = 256;    // MI355X compute units (when no device answers)
+constexpr int kMaxDevices = 64;
 constexpr int kMaxSplits = 16;
 // One uint32 counter per output tile in the workspace's counter area, which
 // has the same size (kCounterBytes) for every shape, so the partial sums of
@@ -27,17 +31,12 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
-int env_int(const char* name, int dflt) {
-    const char* v = getenv(name);
-    if (!v || !*v) return dflt;
-    char* end = nullptr;
-    long x = strtol(v, &end, 10);
-    return (end && *end == 0) ? (int)x : dflt;
-}
-
-// Shape checks shared by every entry point: 0 = ok, else a status.
-w4a16_status_t check_shape(int64_t K, int64_t N, int group_size, uint32_t flags) {
-    if (flags & ~W4A16_FLAGS_MASK) return W4A16_ERR_INVALID_ARG;
+// Shape checks shared by every entry point: 0 = ok, else a status.  Plan
+// hints (W4A16_PLAN_*) are accepted only where a plan is made.
+w4a16_status_t check_shape(int64_t K, int64_t N, int group_size, uint32_t flags,
+                           bool plan_hints = false) {
+    const uint32_t allowed = W4A16_FLAGS_MASK | (plan_hints ? W4A16_PLAN_BITS : 0u);
+    if (flags & ~allowed) return W4A16_ERR_INVALID_ARG;
     if (K < 1 || N < 1 || K >= kMaxDim || N >= kMaxDim) return W4A16_ERR_INVALID_ARG;
     if (group_size != 32 && group_size != 64 && group_size != 128) {
         // a group size that cannot divide K is an invalid request whatever the build
@@ -46,27 +45,72 @@ w4a16_status_t check_shape(int64_t K, int64_t N, int group_size, uint32_t flags)
     }
     if (K % group_size != 0) return W4A16_ERR_INVALID_ARG;
     if ((double)K * (double)N >= (double)((int64_t)1 << 40)) return W4A16_ERR_INVALID_ARG;
-    if (N % kColBlock != 0) return W4A16_ERR_UNSUPPORTED;
+    if (K % kKAlign != 0 || N % kColBlock != 0) return W4A16_ERR_UNSUPPORTED;
     return W4A16_OK;
 }
 
 w4a16_status_t from_hip(hipError_t e) { return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP; }
 
+// Compute units of the current device, asked once per device (kDefaultCUs when
+// no device answers, e.g. a host without a GPU asking for workspace sizes).
+int num_cus() {
+    static std::atomic<int> cache[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return kDefaultCUs;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        n = kDefaultCUs;
+    cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
 }  // namespace
 
-Plan make_plan(int64_t M, int64_t N, int64_t K, int G, uint32_t /*flags*/) {
+Plan make_plan(int64_t M, int64_t N, int64_t K, int G, uint32_t flags) {
     Plan p;
     memset(&p, 0, sizeof(p));
+    const int cus = num_cus();
     const int64_t KS = K / kKStep;
     const int64_t NB = N / kColBlock;
-    const char* fv = getenv("W4A16_FORCE_VARIANT");
-    bool splitk = M <= 32;
-    if (fv && strcmp(fv, "splitk") == 0 && M <= 32) splitk = true;
-    if (fv && strcmp(fv, "tiled") == 0) splitk = false;
-    const int forced_splits = env_int("W4A16_SPLITS", 0);
+    const int64_t NT = N / kTileCols;
+    const uint32_t hint = flags & W4A16_PLAN_MASK;
+    const int param = (int)((flags >> W4A16_PLAN_PARAM_SHIFT) & 0xFFu);
     (void)G;
 
-    if (splitk) {
+    // The decode kernel holds X in LDS: it serves M <= 8 whenever X fits.
+    auto decode_fits = [&](int tpi) {
+        return decode_lds_bytes(M, K, tpi, M <= 8 ? 8 : 32) <= kDecodeLdsMax &&
+               (size_t)M * (size_t)K * 2 <= kDecodeXMax;
+    };
+    Variant v;
+    if (hint == W4A16_PLAN_DECODE && M <= 32 && decode_fits(1))
+        v = VARIANT_DECODE;
+    else if (hint == W4A16_PLAN_SPLITK && M <= 32)
+        v = VARIANT_SPLITK;
+    else if (hint == W4A16_PLAN_TILED)
+        v = VARIANT_TILED;
+    else if (M <= 8 && decode_fits(1))
+        v = VARIANT_DECODE;
+    else if (M <= 32)
+        v = VARIANT_SPLITK;
+    else
+        v = VARIANT_TILED;
+
+    if (v == VARIANT_DECODE) {
+        // Items of one tile over all of K, dealt round-robin to one workgroup
+        // per CU; no workspace.
+        p.variant = VARIANT_DECODE;
+        p.tpi = 1;
+        p.items = (int)NT;
+        p.waves = kDecodeWaves;
+        p.grid_x = (int)std::min<int64_t>(p.items, cus);
+        if (hint == W4A16_PLAN_DECODE && param > 0)   // forced workgroup count
+            p.grid_x = (int)std::min<int64_t>(p.items, param);
+        p.grid_y = 1;
+        p.grid_z = 1;
+        p.splits = 1;
+    } else if (v == VARIANT_SPLITK) {
         // Balanced contiguous ranges of batches for every wave of one
         // workgroup per CU (fewer workgroups when there are fewer batches).
         p.variant = VARIANT_SPLITK;
@@ -79,13 +123,12 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int G, uint32_t /*flags*/) {
         // 3/4 of the CUs; otherwise one workgroup per CU, but at least two
         // batches per wave (small problems pay more for shared tiles than
         // they gain from more CUs).
-        const int64_t per_wg = ceil_div(NB, kNumCUs);          // blocks per workgroup
+        const int64_t per_wg = ceil_div(NB, cus);               // blocks per workgroup
         int64_t W = ceil_div(NB, per_wg);
-        if (W * 4 < kNumCUs * 3) W = kNumCUs;
+        if (W * 4 < (int64_t)cus * 3) W = cus;
         if (W > TB / (2 * p.waves)) W = TB / (2 * p.waves);
         if (W < 1) W = 1;
-        const int forced_wgs = env_int("W4A16_SPLITK_WGS", 0);
-        if (forced_wgs > 0) W = forced_wgs;
+        if (hint == W4A16_PLAN_SPLITK && param > 0) W = (int64_t)param * 8;  // forced: 8*param
         if (W > ceil_div(TB, p.waves)) W = ceil_div(TB, p.waves);   // every workgroup has work
         if (W > kMaxTilesSplit) W = kMaxTilesSplit;                  // counters fit their area
         const int64_t TW = W * p.waves;
@@ -118,11 +161,11 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int G, uint32_t /*flags*/) {
         // as one round of workgroups (one per CU) goes: measured on MI355X, a
         // second round or more partial tiles cost more than they gain.
         int64_t s = 1;
-        if (tiles < kNumCUs) s = kNumCUs / tiles;
+        if (tiles < cus) s = cus / tiles;
         if (s > kMaxSplits) s = kMaxSplits;
-        if (forced_splits > 0) s = forced_splits < kMaxSplits ? forced_splits : kMaxSplits;
-        // at least 4 stages per split
-        int64_t sps = round_up(ceil_div(KS, s), kTiledStage);
+        if (hint == W4A16_PLAN_TILED && param > 0) s = param < kMaxSplits ? param : kMaxSplits;
+        // at least 4 stages per split, and whole bodies (two stages) per split
+        int64_t sps = round_up(ceil_div(KS, s), 2 * kTiledStage);
         if (sps < 4 * kTiledStage) sps = 4 * kTiledStage;
         p.steps_per_split = (int)sps;
         p.splits = (int)ceil_div(KS, sps);
@@ -135,7 +178,7 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int G, uint32_t /*flags*/) {
     if (p.variant == VARIANT_TILED && p.splits > 1 && p.tiles > kMaxTilesSplit) {
         // enough tiles to fill the machine without splitting K
         p.splits = 1;
-        p.steps_per_split = (int)round_up(KS, kTiledStage);
+        p.steps_per_split = (int)round_up(KS, 2 * kTiledStage);
         p.grid_z = 1;
     }
     if (p.splits > 1) {
@@ -156,6 +199,13 @@ namespace w4a16 {
 hipError_t launch_gemm(const void* X, const void* packed, void* Y, int64_t M, const Layout& L,
                        bool bf16, const Plan& plan, void* workspace, const Epilogue& ep,
                        hipStream_t stream) {
+    if (plan.variant == VARIANT_DECODE) {
+        if (bf16)
+            return ep.any ? launch_decode_bf16_ep(X, packed, Y, M, L, plan, ep, stream)
+                          : launch_decode_bf16(X, packed, Y, M, L, plan, ep, stream);
+        return ep.any ? launch_decode_f16_ep(X, packed, Y, M, L, plan, ep, stream)
+                      : launch_decode_f16(X, packed, Y, M, L, plan, ep, stream);
+    }
     if (bf16)
         return ep.any ? launch_gemm_bf16_ep(X, packed, Y, M, L, plan, workspace, ep, stream)
                       : launch_gemm_bf16(X, packed, Y, M, L, plan, workspace, ep, stream);
@@ -167,7 +217,7 @@ w4a16_status_t prepare_gemm(const void* X, const void* packed, size_t packed_byt
                             int64_t M, int64_t N, int64_t K, int group_size, uint32_t flags,
                             const w4a16_epilogue_t* epilogue, GemmCall* out) {
     if (M < 1 || M >= kMaxDim) return W4A16_ERR_INVALID_ARG;
-    w4a16_status_t st = check_shape(K, N, group_size, flags);
+    w4a16_status_t st = check_shape(K, N, group_size, flags, true);
     if (st != W4A16_OK) return st;
     if (!X || !packed || !Y) return W4A16_ERR_INVALID_ARG;
     if (!aligned16(X) || !aligned16(packed) || !aligned16(Y)) return W4A16_ERR_INVALID_ARG;
@@ -273,7 +323,7 @@ w4a16_status_t w4a16_unrepack(const void* packed, size_t packed_bytes, uint32_t*
 }
 
 size_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int group_size, uint32_t flags) {
-    if (M < 1 || M >= kMaxDim || check_shape(K, N, group_size, flags) != W4A16_OK) return 0;
+    if (M < 1 || M >= kMaxDim || check_shape(K, N, group_size, flags, true) != W4A16_OK) return 0;
     return make_plan(M, N, K, group_size, flags).workspace;
 }
 

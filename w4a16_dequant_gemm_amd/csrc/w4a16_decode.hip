@@ -1,0 +1,373 @@
+// w4a16_decode.hip -- the small-M (decode) fused W4A16 dequantize-GEMM kernel
+// for gfx950.
+//
+// Page "W4A16 GEMM 算子浅析" (nxmr.cn), section "硬件性能拐点": at batch 1-8
+// the product is bound by the weight stream; page "量化开销对比"
+// (laojiahuo2003.github.io), section 6.5: the weights are read exactly once,
+// reuse is along N, and the weight bytes divided by the bandwidth are the
+// time floor.  Section 6.2: per output tile, walk along k, unpack each weight
+// word, apply the group scale and zero before the multiply-accumulate, keep
+// the accumulators in registers, with the next loads in flight.
+//
+// Work decomposition.  An item is TPI tiles (32 columns each) over all of K.
+// A workgroup of 8 waves takes items blockIdx.x, blockIdx.x + gridDim.x, ...
+// (one workgroup per CU); its waves split K into equal ranges of bodies (256
+// of K each), so every wave streams contiguous 4 KiB runs of each tile.  An
+// item's partial tiles are added in LDS in wave order and stored by the
+// workgroup itself: no partial sum ever leaves the CU, there is no workspace
+// and nothing waits on another workgroup.
+//
+// Streaming.  Each wave keeps PB bodies of weights (4 KiB per tile each) and
+// their scale/zero entries in flight in registers while it computes the
+// current body, across item boundaries; the loads of a future body are
+// issued unconditionally (a clamped address past the wave's last body) so the
+// compiler can count exactly how many are outstanding.
+//
+// Activations.  X (M rows of K) is copied into LDS once per workgroup, rows
+// padded by 16 bytes so that the rows a quarter-wave reads at one k sit in
+// different banks; the A operand of each k-step is one ds_read_b128 per lane
+// (lane l: row min(l % 32, M - 1), 8 halves at 8 * (l / 32)).  Rows >= M feed
+// only accumulator rows that are never stored.
+//
+// MFMA: v_mfma_f32_32x32x16_{f16,bf16}, one per (k-step, tile); B operand =
+// lane l's dequantized word (column l % 32 of the tile, 8 k at 8 * (l / 32)).
+#include <hip/hip_runtime.h>
+
+#include <type_traits>
+
+#include "w4a16_device.h"
+#include "w4a16_epilogue.h"
+#include "w4a16_internal.h"
+
+#ifndef W4A16_TU_BF16
+#define W4A16_TU_BF16 0
+#endif
+#ifndef W4A16_TU_EP
+#define W4A16_TU_EP 0
+#endif
+
+namespace w4a16 {
+
+namespace {
+
+constexpr int DW = kDecodeWaves;   // waves per workgroup
+
+// LDS barrier that waits for this wave's LDS operations only: global loads
+// stay in flight across it (the compiler waits for each where it is used).
+__device__ __forceinline__ void barrier_lds() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int DT, bool SYM, int G, int MB, int TPI, int PB, bool EP>
+__global__ __launch_bounds__(DW * 64) void decode_kernel(
+    const uint16_t* __restrict__ X, const uint8_t* __restrict__ packed, uint16_t* __restrict__ Y,
+    int M, int N, int K, int n_items, size_t s_off, size_t z_off, size_t t_off, Epilogue ep) {
+    constexpr int EPB = kBodyK / G;          // groups per body: 2, 4, 8
+    constexpr int GS = G / kKStep;           // k-steps per group: 8, 4, 2
+    constexpr int SE = 2 * EPB;              // scale entry bytes
+    constexpr int ZE = EPB / 2;              // zero entry bytes
+    constexpr int QMAX = MB / 8;             // 8-row accumulator groups that can hold rows < M
+    constexpr int R = PB + 1;                // bodies held per wave (ring)
+    extern __shared__ __align__(16) uint8_t lds[];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int KC = K / kChunkK;
+    const int KB = K / kBodyK;
+    const int QM = (M + 7) >> 3;
+    // this wave's bodies of every item: [b0, b0 + nbw)
+    const int bbase = KB / DW, brem = KB % DW;
+    const int b0 = wave * bbase + min(wave, brem);
+    const int nbw = bbase + (wave < brem ? 1 : 0);
+    const int my_items = (n_items - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+    const int nsteps = my_items * nbw;
+
+    // LDS: X rows (row stride RS bytes), the partial-tile slots of two
+    // items, their two arrival counters and two counts of reduced items
+    const int RS = 2 * K + 16;
+    f32x4* slots = (f32x4*)(lds + (size_t)M * RS);   // [2][DW][TPI][QMAX][64]
+    uint32_t* cnt = (uint32_t*)(slots + 2 * DW * TPI * QMAX * 64);
+    auto slot = [&](int par, int w, int tt, int q) -> f32x4& {
+        return slots[(((par * DW + w) * TPI + tt) * QMAX + q) * 64 + lane];
+    };
+    if (tid < 4) cnt[tid] = 0u;
+
+    const bool exact = [&] {
+        if constexpr (DT == DT_F16) {
+            return false;
+        } else {
+            return (*(const uint32_t*)(packed + t_off + 8) & kFlagExactBf16) != 0;
+        }
+    }();
+
+    // ---- one body's loads: TPI tiles x 4 chunks, and their scale/zero entries
+    struct Bundle {
+        u32x4 w[TPI][4];
+        SEnt<G> s[TPI];
+        uint32_t z[TPI];
+    };
+    const uint32_t lane16 = (uint32_t)lane * 16;
+    const int c32 = lane & 31;
+    // issue cursor: item j of this workgroup, body b0 + ib of this wave; past
+    // the last body it stays on the last one (cached, never used).  A wave
+    // without bodies (K below 256 * waves) loads body 0 and never uses it.
+    // Every call issues the same loads, so the compiler counts them exactly.
+    int ij = 0, ib = 0;
+    auto issue = [&](Bundle& B) {
+        const bool real = ij < my_items;
+        const int j = real ? ij : my_items - 1;
+        const int b = nbw == 0 ? 0 : b0 + (real ? ib : nbw - 1);
+        const int item = (int)blockIdx.x + j * (int)gridDim.x;
+#pragma unroll
+        for (int tt = 0; tt < TPI; ++tt) {
+            const int t = item * TPI + tt;
+            const uint8_t* wb = packed + ((size_t)t * KC + 4 * (size_t)b) * kChunkBytes + lane16;
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc)
+                B.w[tt][cc] = __builtin_nontemporal_load((const u32x4*)(wb + cc * kChunkBytes));
+            const size_t ent = ((size_t)t * KB + b) * 32 + c32;
+            B.s[tt] = load_sent<G>(packed + s_off + ent * SE);
+            B.z[tt] = SYM ? 0u : load_zent<G>(packed + z_off + ent * ZE);
+        }
+        if (++ib >= nbw) {
+            ib = 0;
+            ++ij;
+        }
+    };
+
+    // ---- X into LDS, and the first PB bodies' loads, all issued at once: X
+    // first (16-byte pieces, NP per thread with NP the power of two that
+    // covers X -- at most kDecodeXPieces, the LDS budget bounds X -- loaded
+    // unconditionally at clamped addresses so that the compiler counts
+    // exactly how many loads are outstanding), then the bodies; each piece is
+    // written to LDS as soon as it has arrived, which waits for the X loads
+    // only, not for the bodies behind them.  Pieces past the end were loaded
+    // from the last one and are written back to its place (the same bytes).
+    Bundle ring[R];
+    const int vpr = K / 8;                        // 16-byte pieces per row
+    const int nvec = M * vpr;
+    auto stage = [&](auto np_) {
+        constexpr int NP = decltype(np_)::value;
+        u32x4 xv[NP];
+#pragma unroll
+        for (int i = 0; i < NP; ++i)
+            xv[i] = *(const u32x4*)(X + (size_t)min(i * DW * 64 + tid, nvec - 1) * 8);
+        __builtin_amdgcn_sched_barrier(0);   // all X loads, then all body loads
+#pragma unroll
+        for (int i = 0; i < PB; ++i) issue(ring[i]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+            const int v = min(i * DW * 64 + tid, nvec - 1);
+            const int row = v / vpr;
+            *(u32x4*)(lds + (size_t)row * RS + (v - row * vpr) * 16) = xv[i];
+        }
+    };
+    static_assert(kDecodeXPieces == 16, "the piece counts below");
+    const int np = (nvec + DW * 64 - 1) / (DW * 64);
+    if (np <= 1)
+        stage(std::integral_constant<int, 1>{});
+    else if (np <= 2)
+        stage(std::integral_constant<int, 2>{});
+    else if (np <= 4)
+        stage(std::integral_constant<int, 4>{});
+    else if (np <= 8)
+        stage(std::integral_constant<int, 8>{});
+    else
+        stage(std::integral_constant<int, 16>{});
+    barrier_lds();
+
+    // NACC accumulators per tile (k-steps alternate between them), so that
+    // consecutive MFMAs do not wait for each other's result: two for a single
+    // tile, one each when several tiles interleave
+    constexpr int NACC = TPI == 1 ? 2 : 1;
+    f32x16 acc[TPI][NACC];
+#pragma unroll
+    for (int tt = 0; tt < TPI; ++tt)
+#pragma unroll
+        for (int h = 0; h < NACC; ++h) acc[tt][h] = f32x16{};
+
+    const Magic mg = make_magic();
+    const uint32_t zsh = zent_shift<G>(c32);   // this lane's zero entry in its dword
+    // A operand address of this lane: row min(l % 32, M - 1), halves 8 * (l / 32)
+    const uint32_t arow = (uint32_t)min(c32, M - 1) * RS + 16 * (lane >> 5);
+
+    // One body: the 16 A operands are read from LDS first (all in flight
+    // together), then each k-step's words are dequantized and fed to the MFMAs.
+    auto compute = [&](const Bundle& B, int b, auto ex) {
+        const uint8_t* abase = lds + arow + (size_t)b * (kBodyK * 2);
+        u32x4 a[16];
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) a[kk] = *(const u32x4*)(abase + kk * (kKStep * 2));
+        __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the body's work
+        ColParams<DT> prm[TPI];
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int kk = 4 * cc + u;        // k-step inside the body
+                if (kk % GS == 0) {
+                    const int e = kk / GS;
+#pragma unroll
+                    for (int tt = 0; tt < TPI; ++tt)
+                        prm[tt] = entry_params<DT, SYM>(B.s[tt].word(e >> 1), B.z[tt] >> zsh, e);
+                }
+#pragma unroll
+                for (int tt = 0; tt < TPI; ++tt) {
+                    const u32x4 bop = dequant_sel<decltype(ex)::value>(B.w[tt][cc][u], prm[tt], mg);
+                    acc[tt][kk % NACC] = mfma32x32x16<DT>(a[kk], bop, acc[tt][kk % NACC]);
+                }
+            }
+        }
+    };
+
+    // End of item j (the j-th of this workgroup), without a barrier: each wave
+    // writes its partial tiles to the slots of parity j % 2 and bumps that
+    // parity's arrival counter; the wave that arrives last adds the slots in
+    // wave order (bitwise reproducible), runs the epilogue, stores Y, resets
+    // the arrival counter and then bumps that parity's count of reduced items.
+    // LDS operations of one wave complete in order, so a wave's slot writes
+    // precede its arrival and the reducer's slot reads precede its reset.
+    // Before writing the slots of parity j % 2 a wave waits until j / 2 items
+    // of that parity have been reduced, i.e. item j - 2 (whose slots and
+    // counter it reuses); that reducer is a running wave of this workgroup
+    // that waits on nothing, so the wait always ends (and is bounded besides).
+    const int nact = min(DW, KB);                 // waves that own bodies
+    auto item_end = [&](int j) {
+        const int par = j & 1;
+        if (j >= 2) {
+            for (int spin = 0; spin < (1 << 22); ++spin) {
+                const uint32_t d = __builtin_amdgcn_readfirstlane(
+                    __hip_atomic_load(&cnt[2 + par], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+                if (d >= (uint32_t)(j >> 1)) break;
+                __builtin_amdgcn_s_sleep(1);
+            }
+        }
+#pragma unroll
+        for (int tt = 0; tt < TPI; ++tt)
+#pragma unroll
+            for (int q = 0; q < QMAX; ++q)
+                if (q < QM) {
+                    f32x4 v = f32x4{acc[tt][0][4 * q], acc[tt][0][4 * q + 1], acc[tt][0][4 * q + 2],
+                                    acc[tt][0][4 * q + 3]};
+#pragma unroll
+                    for (int h = 1; h < NACC; ++h)
+                        v += f32x4{acc[tt][h][4 * q], acc[tt][h][4 * q + 1], acc[tt][h][4 * q + 2],
+                                   acc[tt][h][4 * q + 3]};
+                    slot(par, wave, tt, q) = v;
+                }
+#pragma unroll
+        for (int tt = 0; tt < TPI; ++tt)
+#pragma unroll
+            for (int h = 0; h < NACC; ++h) acc[tt][h] = f32x16{};
+        // the slot writes are complete (LDS only: loads in flight stay in flight)
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        uint32_t old = 0;
+        if (lane == 0)
+            old = __hip_atomic_fetch_add(&cnt[par], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        old = __builtin_amdgcn_readfirstlane(old);
+        asm volatile("" ::: "memory");
+        if ((int)old != nact - 1) return;
+        const int item = (int)blockIdx.x + j * (int)gridDim.x;
+#pragma unroll
+        for (int tt = 0; tt < TPI; ++tt)
+#pragma unroll
+            for (int q = 0; q < QMAX; ++q) {
+                if (q >= QM) continue;
+                f32x4 v = slot(par, 0, tt, q);
+                for (int w = 1; w < nact; ++w) v += slot(par, w, tt, q);
+                const int64_t col = (int64_t)(item * TPI + tt) * kTileCols + c32;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 8 * q + 4 * (lane >> 5) + i;
+                    if (row < M) Y[(int64_t)row * N + col] = out_value<DT, EP>(v[i], row, col, N, ep);
+                }
+            }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // slot reads done
+        if (lane == 0) {
+            __hip_atomic_store(&cnt[par], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            __hip_atomic_fetch_add(&cnt[2 + par], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+    };
+
+    auto mainloop = [&](auto ex) {
+        if (nbw == 0) return;                     // fewer bodies than waves: nothing to do
+        int j = 0, bb = 0;                        // item and body of step st
+        for (int st = 0; st < nsteps; st += R) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                issue(ring[(r + PB) % R]);
+                if (st + r < nsteps) {
+                    compute(ring[r], b0 + bb, ex);
+                    if (++bb == nbw) {
+                        item_end(j);
+                        bb = 0;
+                        ++j;
+                    }
+                }
+            }
+        }
+    };
+    if (exact)
+        mainloop(std::true_type{});
+    else
+        mainloop(std::false_type{});
+}
+
+template <int DT, bool SYM, int G, int MB, int TPI, int PB>
+hipError_t launch_decode_t(const void* X, const void* packed, void* Y, int64_t M,
+                           const Layout& L, const Plan& p, const Epilogue& ep,
+                           hipStream_t stream) {
+    constexpr bool EPF = W4A16_TU_EP != 0;
+    const size_t lds = decode_lds_bytes(M, L.K, TPI, MB);
+    auto kern = decode_kernel<DT, SYM, G, MB, TPI, PB, EPF>;
+    hipLaunchKernelGGL(kern, dim3(p.grid_x), dim3(DW * 64), lds, stream, (const uint16_t*)X,
+                       (const uint8_t*)packed, (uint16_t*)Y, (int)M, (int)L.N, (int)L.K,
+                       p.items, L.s_off, L.z_off, L.t_off, ep);
+    return hipGetLastError();
+}
+
+template <int DT, bool SYM, int G>
+hipError_t launch_decode_g(const void* X, const void* packed, void* Y, int64_t M,
+                           const Layout& L, const Plan& p, const Epilogue& ep,
+                           hipStream_t stream) {
+    constexpr int PB = kDecodePrefetch;
+    if (M <= 8) return launch_decode_t<DT, SYM, G, 8, 1, PB>(X, packed, Y, M, L, p, ep, stream);
+    return launch_decode_t<DT, SYM, G, 32, 1, PB>(X, packed, Y, M, L, p, ep, stream);
+}
+
+template <int DT, bool SYM>
+hipError_t launch_decode_s(const void* X, const void* packed, void* Y, int64_t M,
+                           const Layout& L, const Plan& p, const Epilogue& ep,
+                           hipStream_t stream) {
+    if (L.G == 128) return launch_decode_g<DT, SYM, 128>(X, packed, Y, M, L, p, ep, stream);
+    if (L.G == 64) return launch_decode_g<DT, SYM, 64>(X, packed, Y, M, L, p, ep, stream);
+    return launch_decode_g<DT, SYM, 32>(X, packed, Y, M, L, p, ep, stream);
+}
+
+}  // namespace
+
+#if W4A16_TU_BF16
+#if W4A16_TU_EP
+#define W4A16_DECODE_ENTRY launch_decode_bf16_ep
+#else
+#define W4A16_DECODE_ENTRY launch_decode_bf16
+#endif
+#else
+#if W4A16_TU_EP
+#define W4A16_DECODE_ENTRY launch_decode_f16_ep
+#else
+#define W4A16_DECODE_ENTRY launch_decode_f16
+#endif
+#endif
+
+hipError_t W4A16_DECODE_ENTRY(const void* X, const void* packed, void* Y, int64_t M,
+                              const Layout& L, const Plan& p, const Epilogue& ep,
+                              hipStream_t stream) {
+    constexpr int DT = W4A16_TU_BF16 ? DT_BF16 : DT_F16;
+    if (L.sym) return launch_decode_s<DT, true>(X, packed, Y, M, L, p, ep, stream);
+    return launch_decode_s<DT, false>(X, packed, Y, M, L, p, ep, stream);
+}
+
+}  // namespace w4a16

@@ -102,16 +102,27 @@ __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t g) {
     return r;
 }
 
+// The two fp16 exponent-bias patterns of the unpack (1024 and 64 in both
+// halves), held in VGPRs the compiler treats as unknown values: made once per
+// kernel and passed to every dequant_word, so they are not re-materialised
+// for each word.
+struct Magic {
+    uint32_t a;   // 0x64006400: fp16 1024, spacing 1
+    uint32_t b;   // 0x54005400: fp16 64, spacing 1/16
+};
+__device__ __forceinline__ Magic make_magic() { return Magic{opaque_v(0x64006400u), opaque_v(0x54005400u)}; }
+
 // Eight dequantized weights of one repacked word as the four dwords of an
 // MFMA operand: dword i holds (j = 2i, j = 2i+1) in its (low, high) halves.
 // 13 VALU instructions: 1 shift, 4 v_and_or_b32, 4 v_pk_add_f16, 4 v_pk_mul_f16.
-__device__ __forceinline__ u32x4 dequant_word(uint32_t w, const ColParams<DT_F16>& p) {
+__device__ __forceinline__ u32x4 dequant_word(uint32_t w, const ColParams<DT_F16>& p,
+                                              const Magic& mg) {
     const uint32_t w8 = w >> 8;
     const f16x2 s2 = __builtin_bit_cast(f16x2, p.s2);
     const f16x2 bA = __builtin_bit_cast(f16x2, p.bA);
     const f16x2 bB = __builtin_bit_cast(f16x2, p.bB);
-    const uint32_t gA = opaque_v(0x64006400u);   // fp16 1024 in both halves
-    const uint32_t gB = opaque_v(0x54005400u);   // fp16 64 in both halves
+    const uint32_t gA = mg.a;   // fp16 1024 in both halves
+    const uint32_t gB = mg.b;   // fp16 64 in both halves
     // nibble positions (0,4) -> j (0,1); (1,5) -> (2,3); (2,6) -> (4,5); (3,7) -> (6,7)
     const f16x2 v0 = __builtin_bit_cast(f16x2, and_or(w, 0x000F000Fu, gA));    // 1024 + q
     const f16x2 v1 = __builtin_bit_cast(f16x2, and_or(w, 0x00F000F0u, gB));    // 64 + q
@@ -132,12 +143,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
-__device__ __forceinline__ u32x4 dequant_word(uint32_t w, const ColParams<DT_BF16>& p) {
+__device__ __forceinline__ u32x4 dequant_word(uint32_t w, const ColParams<DT_BF16>& p,
+                                              const Magic& mg) {
     // The same four (j, j+1) pairs as the fp16 form, each half widened inside
     // the fma (v_fma_mix_f32): 1 shift, 4 v_and_or_b32, 8 fma, 4 cvt.
     const uint32_t w8 = w >> 8;
-    const uint32_t gA = opaque_v(0x64006400u);   // fp16 1024 in both halves
-    const uint32_t gB = opaque_v(0x54005400u);   // fp16 64 in both halves
+    const uint32_t gA = mg.a;   // fp16 1024 in both halves
+    const uint32_t gB = mg.b;   // fp16 64 in both halves
     const f16x2 v0 = __builtin_bit_cast(f16x2, and_or(w, 0x000F000Fu, gA));    // 1024 + q
     const f16x2 v1 = __builtin_bit_cast(f16x2, and_or(w, 0x00F000F0u, gB));    // 64 + q
     const f16x2 v2 = __builtin_bit_cast(f16x2, and_or(w8, 0x000F000Fu, gA));
@@ -158,11 +170,13 @@ __device__ __forceinline__ bool needs_exact_path(const ColParams<DT_BF16>& p) {
     return __builtin_isinf(p.cA);
 }
 
-__device__ __forceinline__ u32x4 dequant_word_exact(uint32_t w, const ColParams<DT_F16>& p) {
-    return dequant_word(w, p);   // the fp16 form is exact for every scale
+__device__ __forceinline__ u32x4 dequant_word_exact(uint32_t w, const ColParams<DT_F16>& p,
+                                                    const Magic& mg) {
+    return dequant_word(w, p, mg);   // the fp16 form is exact for every scale
 }
 
-__device__ __forceinline__ u32x4 dequant_word_exact(uint32_t w, const ColParams<DT_BF16>& p) {
+__device__ __forceinline__ u32x4 dequant_word_exact(uint32_t w, const ColParams<DT_BF16>& p,
+                                                    const Magic&) {
     float v[8];
 #pragma unroll
     for (int p_ = 0; p_ < 8; ++p_) {
@@ -178,21 +192,73 @@ __device__ __forceinline__ u32x4 dequant_word_exact(uint32_t w, const ColParams<
 }
 
 template <bool EXACT, int DT>
-__device__ __forceinline__ u32x4 dequant_sel(uint32_t w, const ColParams<DT>& p) {
+__device__ __forceinline__ u32x4 dequant_sel(uint32_t w, const ColParams<DT>& p, const Magic& mg) {
     if constexpr (EXACT)
-        return dequant_word_exact(w, p);
+        return dequant_word_exact(w, p, mg);
     else
-        return dequant_word(w, p);
+        return dequant_word(w, p, mg);
 }
 
-// Column constants for column tile t (0..3) of a lane, from its scale record
-// entry (four 16-bit scales) and zero record entry (four nibbles).
+// Constants of group entry e of a lane's scale / zero record entries: the
+// scale is 16-bit field e % 2 of `sword` (the record dword that holds entry e)
+// and the zero point is nibble e of `zword` (8 for the symmetric format).
 template <int DT, bool SYM>
-__device__ __forceinline__ ColParams<DT> tile_params(u32x2 sc, uint32_t zw, int t) {
-    const uint32_t word = (t < 2) ? sc.x : sc.y;
-    const uint32_t sbits = (t & 1) ? (word >> 16) : (word & 0xFFFFu);
-    const uint32_t z = SYM ? 8u : ((zw >> (4 * t)) & 0xFu);
+__device__ __forceinline__ ColParams<DT> entry_params(uint32_t sword, uint32_t zword, int e) {
+    const uint32_t sbits = (e & 1) ? (sword >> 16) : (sword & 0xFFFFu);
+    const uint32_t z = SYM ? 8u : ((zword >> (4 * e)) & 0xFu);
     return col_params<DT>(sbits, z);
+}
+
+// Scale entry of a lane for one body: 256/G scales (4, 8 or 16 bytes).
+template <int G>
+struct SEnt;
+template <>
+struct SEnt<128> {
+    uint32_t v;
+    __device__ uint32_t word(int) const { return v; }
+};
+template <>
+struct SEnt<64> {
+    u32x2 v;
+    __device__ uint32_t word(int i) const { return v[i]; }
+};
+template <>
+struct SEnt<32> {
+    u32x4 v;
+    __device__ uint32_t word(int i) const { return v[i]; }
+};
+
+template <int G>
+__device__ __forceinline__ SEnt<G> load_sent(const uint8_t* p) {
+    SEnt<G> s;
+    if constexpr (G == 128)
+        s.v = *(const uint32_t*)p;
+    else if constexpr (G == 64)
+        s.v = *(const u32x2*)p;
+    else
+        s.v = *(const u32x4*)p;
+    return s;
+}
+
+// Zero entry of a lane for one body: 256/G nibbles (1, 2 or 4 bytes), read as
+// the aligned dword that holds it (sub-dword loads make the compiler insert
+// zero-extensions that wait for every load in flight).  The entry sits at bit
+// zent_shift<G>(c32) of that dword.
+template <int G>
+__device__ __forceinline__ uint32_t load_zent(const uint8_t* p) {
+    // pointer arithmetic (not an integer round trip) keeps the global address
+    // space, so this stays a global load (a flat load is waited for with
+    // vmcnt(0), i.e. after every load in flight)
+    return *(const uint32_t*)(p - ((uintptr_t)p & 3));
+}
+template <int G>
+__device__ __forceinline__ uint32_t zent_shift(int c32) {
+    if constexpr (G == 128)
+        return 8u * (uint32_t)(c32 & 3);
+    else if constexpr (G == 64)
+        return 16u * (uint32_t)(c32 & 1);
+    else
+        return 0u;
 }
 
 // D = A.B + C on one 32x32x16 tile.  A: lane l holds row l%32, reduction

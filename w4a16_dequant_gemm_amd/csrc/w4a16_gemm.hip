@@ -38,6 +38,7 @@
 #include <type_traits>
 
 #include "w4a16_device.h"
+#include "w4a16_epilogue.h"
 #include "w4a16_internal.h"
 
 // This file is compiled once per (activation dtype, epilogue) pair, each
@@ -97,42 +98,6 @@ __device__ __forceinline__ bool uses_exact_form(const uint8_t* packed, size_t t_
         const uint32_t flags = *(const uint32_t*)(packed + t_off + 8);
         return (flags & kFlagExactBf16) != 0;
     }
-}
-
-// ---------------------------------------------------------------------------
-// Output epilogue, run on the fp32 accumulator just before its one store.
-// Page "量化开销对比", sections 6.2, 6.6 and 6.7: after the k loop the result
-// is scaled per output channel, the bias added, and a residual or activation
-// applied inside the same kernel, so no further launch re-reads Y.  Each
-// step is optional; the order is t = v*c[n] + b[n], u = act(t), then
-// u + a[m][n] or u * a[m][n].  All in fp32, one rounding into the output dtype.
-// ---------------------------------------------------------------------------
-template <int DT>
-__device__ __forceinline__ float act_in(uint16_t b) {
-    if constexpr (DT == DT_F16)
-        return (float)__builtin_bit_cast(_Float16, b);
-    else
-        return __uint_as_float((uint32_t)b << 16);
-}
-
-// EP = false: the plain store.  EP = true: every pointer of ep is valid (the
-// host substitutes a harmless source for an absent operand), so each element
-// runs the same straight-line code: unconditional loads, then selects.
-template <int DT, bool EP>
-__device__ __forceinline__ uint16_t out_value(float v, int64_t row, int64_t col, int N,
-                                              const Epilogue& ep) {
-    if constexpr (EP) {
-        const float c = ep.has_scale ? ep.col_scale[col] : 1.0f;
-        const float b = ep.has_bias ? act_in<DT>(ep.bias[col]) : 0.0f;
-        const float a = act_in<DT>(ep.aux[row * N + col]);
-        const float t = v * c + b;
-        // SiLU as t * 1/(1 + 2^(-t*log2 e)) with the hardware exp2 and reciprocal
-        const float sg =
-            t * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-t * 1.4426950408889634f));
-        const float u = ep.act == kActSilu ? sg : (ep.act == kActRelu ? (t > 0.0f ? t : 0.0f) : t);
-        v = ep.has_aux ? (ep.aux_mul ? u * a : u + a) : u;
-    }
-    return round_out<DT>(v);
 }
 
 // ---------------------------------------------------------------------------
@@ -238,15 +203,18 @@ __global__ __launch_bounds__(SK_WAVES * 64) void splitk_kernel(
     const uint16_t* __restrict__ X, const uint8_t* __restrict__ packed, uint16_t* __restrict__ Y,
     float* __restrict__ part, uint32_t* __restrict__ cnt, int M, int N, int K, int nbat, int base,
     int rem, size_t s_off, size_t z_off, size_t t_off, Epilogue ep) {
-    constexpr int SPG = GS < SK_U ? GS : SK_U;   // k-steps per group inside a batch
-    constexpr int NGB = SK_U / SPG;              // groups (or group parts) per batch
+    constexpr int G = GS * kKStep;               // group size
+    constexpr int EPB = kBodyK / G;              // groups per body
+    constexpr int SE = 2 * EPB;                  // scale entry bytes
+    constexpr int ZE = EPB / 2;                  // zero entry bytes
     constexpr int QMAX = MB / 8;                 // 8-row accumulator groups that can hold rows < M
+    static_assert(SK_U == kChunkK / kKStep, "a batch is one chunk of each tile of the block");
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int wg = blockIdx.x;
-    const int KS = K / kKStep;
-    const int NG = K / (kKStep * GS);
+    const int KC = K / kChunkK;
+    const int KB = K / kBodyK;
     const int QM = (M + 7) >> 3;
     const int gw = wg * SK_WAVES + wave;
     const int s_w = range_start(gw, base, rem);
@@ -262,43 +230,39 @@ __global__ __launch_bounds__(SK_WAVES * 64) void splitk_kernel(
     // feed accumulator rows that are never stored), 8 halves at 8*(lane/32).
     const int arow = min(lane & 31, M - 1);
     const uint16_t* xlane = X + (size_t)arow * K + 8 * (lane >> 5);
-    const uint8_t* srec = packed + s_off + (lane & 31) * 8;
-    const uint8_t* zrec = packed + z_off + (lane & 31) * 2;
+    const int c32 = lane & 31;
+    const uint32_t lane16 = (uint32_t)lane * 16;
 
+    // Batch i of block nb: chunk i (k-steps 4i..4i+3) of each of the block's
+    // four tiles, and the scale/zero entries of the body that holds it.
     struct Batch {
-        u32x4 w[SK_U];
-        u32x4 x[SK_U];
-        u32x2 sc[NGB];
-        uint32_t zw[NGB];
+        u32x4 w[4];          // tile t's chunk: word u = k-step u
+        u32x4 x[SK_U];       // A operand of k-step u
+        SEnt<G> s[4];
+        uint32_t z[4];
     };
 
     // Loads of one batch, all unconditional so that the compiler can count
     // exactly how many are still in flight.  Past the end of the range they
     // read cache-resident data instead (the lane's activations and the first
-    // scale/zero record; values never used), so that the final wait for
+    // scale/zero entries; values never used), so that the final wait for
     // outstanding loads does not wait for HBM.
     const int hb = s_w / nbat, ib = s_w - hb * nbat;   // first batch: block, batch in block
     int nbL = hb, iL = ib, issued = 0;
     auto issue = [&](Batch& b) {
         const bool real = issued < len;
-        const int ks0 = real ? iL * SK_U : 0;
-        const int nv = real ? min(SK_U, KS - ks0) : 1;
-        const size_t chunk0 = real ? (size_t)nbL * KS + ks0 : 0;
-        const size_t rec0 = real ? (size_t)nbL * NG + ks0 / GS : 0;
+        const int c = real ? iL : 0;
 #pragma unroll
-        for (int q = 0; q < NGB; ++q) {
-            const size_t rec = rec0 + (size_t)min(q * SPG, nv - 1) / GS;
-            b.sc[q] = *(const u32x2*)(srec + rec * kScaleRecBytes);
-            b.zw[q] = SYM ? 0u : (uint32_t)*(const uint16_t*)(zrec + rec * kZeroRecBytes);
+        for (int t = 0; t < 4; ++t) {
+            const size_t tile = real ? (size_t)4 * nbL + t : 0;
+            const size_t ent = (tile * KB + (c >> 2)) * 32 + c32;
+            b.s[t] = load_sent<G>(packed + s_off + ent * SE);
+            b.z[t] = SYM ? 0u : load_zent<G>(packed + z_off + ent * ZE);
+            b.w[t] = load_weights(real ? (const u32x4*)(packed + (tile * KC + c) * kChunkBytes + lane16)
+                                       : (const u32x4*)xlane);
         }
-        const u32x4* wsrc = real ? (const u32x4*)packed + chunk0 * 64 + lane : (const u32x4*)xlane;
-        const int wstep = real ? 64 : 0;
 #pragma unroll
-        for (int u = 0; u < SK_U; ++u) {
-            const int uu = min(u, nv - 1);
-            b.w[u] = load_weights(wsrc + uu * wstep);
-            b.x[u] = *(const u32x4*)(xlane + (size_t)(ks0 + uu) * kKStep);
-        }
+        for (int u = 0; u < SK_U; ++u) b.x[u] = *(const u32x4*)(xlane + (size_t)(4 * c + u) * kKStep);
         ++issued;
         if (++iL == nbat) {
             iL = 0;
@@ -309,23 +273,25 @@ __global__ __launch_bounds__(SK_WAVES * 64) void splitk_kernel(
     f32x16 acc[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[t] = f32x16{};
+    const Magic mg = make_magic();
+    const uint32_t zsh = zent_shift<G>(c32);   // this lane's zero entry in its dword
 
-    auto compute = [&](const Batch& b, int nv, auto ex) {
+    // k-step u of batch i is k-step 4*(i % 4) + u of its body: group entry
+    // (4*(i % 4) + u) / GS of the body's scale/zero entries.
+    auto compute = [&](const Batch& b, int i, auto ex) {
+        ColParams<DT> prm[4];
 #pragma unroll
-        for (int q = 0; q < NGB; ++q) {
-            if (q * SPG >= nv) break;
-            ColParams<DT> prm[4];
+        for (int u = 0; u < SK_U; ++u) {
+            if (u % GS == 0) {
+                const int e = (4 * (i & 3) + u) / GS;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) prm[t] = tile_params<DT, SYM>(b.sc[q], b.zw[q], t);
+                for (int t = 0; t < 4; ++t)
+                    prm[t] = entry_params<DT, SYM>(b.s[t].word(e >> 1), b.z[t] >> zsh, e);
+            }
 #pragma unroll
-            for (int uu = 0; uu < SPG; ++uu) {
-                const int u = q * SPG + uu;
-                if (u >= nv) break;
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const u32x4 bop = dequant_sel<decltype(ex)::value>(b.w[u][t], prm[t]);
-                    acc[t] = mfma32x32x16<DT>(b.x[u], bop, acc[t]);
-                }
+            for (int t = 0; t < 4; ++t) {
+                const u32x4 bop = dequant_sel<decltype(ex)::value>(b.w[t][u], prm[t], mg);
+                acc[t] = mfma32x32x16<DT>(b.x[u], bop, acc[t]);
             }
         }
     };
@@ -394,7 +360,7 @@ __global__ __launch_bounds__(SK_WAVES * 64) void splitk_kernel(
             for (int r = 0; r < SK_NBUF; ++r) {
                 issue(bf[(r + SK_NBUF - 1) % SK_NBUF]);
                 if (b < len) {
-                    compute(bf[r], min(SK_U, KS - iC * SK_U), ex);
+                    compute(bf[r], iC, ex);
                     const bool block_end = iC == nbat - 1;
                     const bool range_end = b == len - 1;
                     if (block_end || range_end) {
@@ -536,7 +502,7 @@ __global__ __launch_bounds__(SK_WAVES * 64) void splitk_kernel(
 // ---------------------------------------------------------------------------
 constexpr int TK_WAVES = 8;
 
-template <int DT, bool SYM, int GS, int MT, bool FULL, bool EP>
+template <int DT, bool SYM, int GS, int MT, bool EP>
 __global__ __launch_bounds__(TK_WAVES * 64) void tiled_kernel(
     const uint16_t* __restrict__ X, const uint8_t* __restrict__ packed, uint16_t* __restrict__ Y,
     float* __restrict__ part, uint32_t* __restrict__ cnt, int M, int N, int K,
@@ -561,22 +527,29 @@ __global__ __launch_bounds__(TK_WAVES * 64) void tiled_kernel(
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int half = wave >> 2;                 // column tiles 2*half, 2*half+1 of the block
+    constexpr int G = GS * kKStep;              // group size
+    constexpr int EPB = kBodyK / G;             // groups per body
+    constexpr int SE = 2 * EPB;                 // scale entry bytes (a body)
+    constexpr int ZE = EPB / 2;                 // zero entry bytes (a body)
     const int NB = N / kColBlock;
     const int KS = K / kKStep;
-    const int NG = K / (kKStep * GS);
+    const int KC = K / kChunkK;
+    const int KB = K / kBodyK;
     const int nb = blockIdx.x * 4 + (wave & 3);
     const bool nb_ok = nb < NB;
     const int nbc = nb_ok ? nb : NB - 1;
     const int m0 = blockIdx.y * ROWS;
     const int split = blockIdx.z;
-    const int s_beg = split * steps_per_split;   // a multiple of KT
+    const int s_beg = split * steps_per_split;   // a multiple of 2*KT (a body)
     const int s_end = min(KS, s_beg + steps_per_split);
-    const int nst = s_end > s_beg ? (s_end - s_beg + KT - 1) / KT : 0;
+    const int nst = s_end > s_beg ? (s_end - s_beg) / KT : 0;
 
-    // this wave's two weight words of each chunk: bytes 8*half..+7 of the lane's 16
-    const u32x2* wbase = (const u32x2*)(packed + (size_t)nbc * KS * 1024 + lane * 16 + half * 8);
-    const uint8_t* srec = packed + s_off + (size_t)nbc * NG * kScaleRecBytes + (lane & 31) * 8 + half * 4;
-    const uint8_t* zrec = packed + z_off + (size_t)nbc * NG * kZeroRecBytes + (lane & 31) * 2;
+    // this wave's two tiles: 4*nb + 2*half + tt; chunk c of tile t at
+    // (t*KC + c) KiB, lane l's 16 bytes at l*16
+    const size_t tile0 = (size_t)4 * nbc + 2 * half;
+    const uint8_t* wbase = packed + tile0 * KC * kChunkBytes + (uint32_t)lane * 16;
+    const uint8_t* sbase = packed + s_off + (tile0 * KB * 32 + (lane & 31)) * SE;
+    const uint8_t* zbase = packed + z_off + (tile0 * KB * 32 + (lane & 31)) * ZE;
 
     // Activation copies: copy i of this thread covers slot
     // s = (8*i + wave)*64 + lane, i.e. row s/16 (rows >= M re-read row M-1,
@@ -612,28 +585,46 @@ __global__ __launch_bounds__(TK_WAVES * 64) void tiled_kernel(
         load_to_lds16(xrow[i] + x_col(si), &buf[(TK_WAVES * i + wave) * 64]);
     };
 
+    // One stage (KT = 8 k-steps, half a body): chunks 2c', 2c'+1 of both tiles
+    // (c' = the stage's index), the stage's scales and the tiles' zero entries
+    // of the body.  Scales: G = 128, the body's two (the stage uses half
+    // `par`); G = 64 and 32, the stage's half of the body entry (2 or 4
+    // scales).  All loads are dword-aligned (see load_zent).
     struct Stage {
-        uint32_t sc[NGST];
-        uint32_t zw[NGST];
-        u32x2 w[KT];
+        uint32_t sc[2][NGST > 2 ? 2 : 1];   // scale dwords of tile tt (two scales each)
+        uint32_t zw[2];                      // the dword holding tile tt's zero entry
+        u32x4 w[2][2];                       // [tile][chunk]: word u = k-step u of the chunk
     };
-    auto load_w_part = [&](Stage& b, int si, int u) {
-        const int st = s_beg + min(si, nst - 1) * KT;
-        if (u == 0) {
+    auto load_w_part = [&](Stage& b, int si, int part) {
+        const int st = s_beg + min(si, nst - 1) * KT;   // first k-step of the stage
+        const int tt = part & 1, cc = part >> 1;
+        if (part == 0) {
+            const int body = st >> 4, par = (st >> 3) & 1;
 #pragma unroll
-            for (int j = 0; j < NGST; ++j) {
-                const int g = min(st + j * SPG, s_end - 1) / GS;
-                b.sc[j] = *(const uint32_t*)(srec + (size_t)g * kScaleRecBytes);
-                b.zw[j] = SYM ? 0u : (uint32_t)*(const uint16_t*)(zrec + (size_t)g * kZeroRecBytes);
+            for (int t = 0; t < 2; ++t) {
+                const uint8_t* se = sbase + ((size_t)t * KB + body) * 32 * SE;
+                if constexpr (NGST == 1) {
+                    b.sc[t][0] = *(const uint32_t*)se;
+                } else if constexpr (NGST == 2) {
+                    b.sc[t][0] = *(const uint32_t*)(se + par * (SE / 2));
+                } else {
+                    const u32x2 v = *(const u32x2*)(se + par * (SE / 2));
+                    b.sc[t][0] = v.x;
+                    b.sc[t][NGST > 2 ? 1 : 0] = v.y;
+                }
+                b.zw[t] = SYM ? 0u : load_zent<G>(zbase + ((size_t)t * KB + body) * 32 * ZE);
             }
         }
-        b.w[u] = __builtin_nontemporal_load(wbase + (size_t)min(st + u, s_end - 1) * 128);
+        b.w[tt][cc] = __builtin_nontemporal_load(
+            (const u32x4*)(wbase + ((size_t)tt * KC + (st >> 2) + cc) * kChunkBytes));
     };
     auto load_w = [&](Stage& b, int si) {
 #pragma unroll
-        for (int u = 0; u < KT; ++u) load_w_part(b, si, u);
+        for (int p = 0; p < 4; ++p) load_w_part(b, si, p);
     };
 
+    const Magic mg = make_magic();
+    const uint32_t zsh = zent_shift<G>(lane & 31);   // this lane's zero entry in its dword
     f32x16 acc[MT][2];
 #pragma unroll
     for (int r = 0; r < MT; ++r)
@@ -655,43 +646,24 @@ __global__ __launch_bounds__(TK_WAVES * 64) void tiled_kernel(
     // MFMAs, and the other wave on the SIMD fills the rest.  issue(u) issues
     // part u of a later stage's loads.
     auto compute = [&](const Stage& b, const u32x4* buf, int si, auto exact, auto issue) {
-        const int nvalid = min(KT, s_end - (s_beg + si * KT));   // <= 0 past the end
         auto read_a = [&](u32x4 (&a)[MT], int u) {
 #pragma unroll
             for (int r = 0; r < MT; ++r) a[r] = buf[arow + 32 * CPR * r + ((2 * u) ^ aswz)];
         };
+        const int par = ((s_beg + si * KT) >> 3) & 1;   // stage inside its body
         auto make_b1 = [&](int u, int tt) {
-            const int j = u / SPG;
-            const u32x2 sc2 = {b.sc[j], b.sc[j]};
-            const ColParams<DT> prm = tile_params<DT, SYM>(sc2, b.zw[j], 2 * half + tt);
-            return dequant_sel<decltype(exact)::value>(b.w[u][tt], prm);
+            const int j = u / SPG;                 // group of k-step u inside the stage
+            const uint32_t sw = NGST == 1 ? b.sc[tt][0] >> (16 * par) : b.sc[tt][j >> 1];
+            const uint32_t zw = SYM ? 0u : b.zw[tt] >> (zsh + 4 * NGST * par);
+            const ColParams<DT> prm = entry_params<DT, SYM>(sw, zw, NGST == 1 ? 0 : j);
+            return dequant_sel<decltype(exact)::value>(b.w[tt][u >> 2][u & 3], prm, mg);
         };
-        if (FULL && nvalid <= 0) return;   // a stage past the last one: nothing to do
+        if (si >= nst) return;   // a stage past the last one: nothing to do
         u32x4 a[MT], bo[2];
         read_a(a, 0);
         bo[0] = make_b1(0, 0);
         bo[1] = make_b1(0, 1);
-        if constexpr (!FULL) {
-            // K not a multiple of the stage: the plain order, which stops after
-            // the last k-step of the split
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int u = 0; u < KT; ++u) issue(u);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int u = 0; u < KT; ++u) {
-                if (u >= nvalid) break;
-                if (u > 0) {
-                    read_a(a, u);
-                    bo[0] = make_b1(u, 0);
-                    bo[1] = make_b1(u, 1);
-                }
-#pragma unroll
-                for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                    for (int r = 0; r < MT; ++r) acc[r][tt] = mfma32x32x16<DT>(a[r], bo[tt], acc[r][tt]);
-            }
-        } else {
+        {
 #pragma unroll
             for (int u = 0; u < KT; ++u) {
                 __builtin_amdgcn_sched_barrier(0);
@@ -759,10 +731,7 @@ __global__ __launch_bounds__(TK_WAVES * 64) void tiled_kernel(
 #pragma unroll
                     for (int i = 0; i < XI; ++i) load_x_part(si, i);
                 }
-                if (2 * u < KT) {
-                    load_w_part(w, si, 2 * u);
-                    load_w_part(w, si, 2 * u + 1);
-                }
+                if (u < 4) load_w_part(w, si, u);
             };
             int i = 0;
             do {
@@ -786,10 +755,7 @@ __global__ __launch_bounds__(TK_WAVES * 64) void tiled_kernel(
             // second half to arrive before the barrier that ends the stage
             auto part = [&](u32x4* to, int si, Stage& w, int u) {
                 if (u < XI) copy_x_part(to, si, u);
-                if (2 * u < KT) {
-                    load_w_part(w, si, 2 * u);
-                    load_w_part(w, si, 2 * u + 1);
-                }
+                if (u < 4) load_w_part(w, si, u);
             };
             int i = 0;
             do {
@@ -938,31 +904,23 @@ void launch_splitk(const void* X, const void* packed, void* Y, int64_t M, const 
     else launch_splitk_mb<DT, SYM, GS, 32>(X, packed, Y, M, L, p, part, cnt, stream, ep);
 }
 
-template <int DT, bool SYM, int GS, int MT, bool FULL>
+template <int DT, bool SYM, int GS, int MT>
 void launch_tiled_mt(const void* X, const void* packed, void* Y, int64_t M, const Layout& L,
                      const Plan& p, float* part, uint32_t* cnt, hipStream_t stream,
-                   const Epilogue& ep) {
-    hipLaunchKernelGGL((tiled_kernel<DT, SYM, GS, MT, FULL, W4A16_TU_EP != 0>),
+                     const Epilogue& ep) {
+    hipLaunchKernelGGL((tiled_kernel<DT, SYM, GS, MT, W4A16_TU_EP != 0>),
                        dim3(p.grid_x, p.grid_y, p.grid_z), dim3(TK_WAVES * 64), 0, stream,
                        (const uint16_t*)X, (const uint8_t*)packed, (uint16_t*)Y, part, cnt, (int)M,
                        (int)L.N, (int)L.K, p.steps_per_split, p.splits, L.s_off, L.z_off, L.t_off,
                        ep);
 }
 
-// FULL: every stage of every split has all its k-steps (K a multiple of the
-// stage depth, 128), which the interleaved schedule assumes.
 template <int DT, bool SYM, int GS>
 void launch_tiled(const void* X, const void* packed, void* Y, int64_t M, const Layout& L,
                   const Plan& p, float* part, uint32_t* cnt, hipStream_t stream,
-                   const Epilogue& ep) {
-    const bool full = (L.K / kKStep) % kTiledStage == 0;
-    if (p.mt == 2) {
-        if (full) launch_tiled_mt<DT, SYM, GS, 2, true>(X, packed, Y, M, L, p, part, cnt, stream, ep);
-        else launch_tiled_mt<DT, SYM, GS, 2, false>(X, packed, Y, M, L, p, part, cnt, stream, ep);
-    } else {
-        if (full) launch_tiled_mt<DT, SYM, GS, 4, true>(X, packed, Y, M, L, p, part, cnt, stream, ep);
-        else launch_tiled_mt<DT, SYM, GS, 4, false>(X, packed, Y, M, L, p, part, cnt, stream, ep);
-    }
+                  const Epilogue& ep) {
+    if (p.mt == 2) launch_tiled_mt<DT, SYM, GS, 2>(X, packed, Y, M, L, p, part, cnt, stream, ep);
+    else launch_tiled_mt<DT, SYM, GS, 4>(X, packed, Y, M, L, p, part, cnt, stream, ep);
 }
 
 template <int DT, bool SYM>

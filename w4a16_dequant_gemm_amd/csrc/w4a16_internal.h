@@ -10,12 +10,34 @@
 
 namespace w4a16 {
 
-enum Variant { VARIANT_SPLITK = 0, VARIANT_TILED = 1 };
+// The split-K and tiled kernels work on column blocks of four tiles.
+constexpr int kColBlock = 4 * kTileCols;
+
+enum Variant { VARIANT_SPLITK = 0, VARIANT_TILED = 1, VARIANT_DECODE = 2 };
 
 // Split-K kernel geometry, shared by the plan and the kernel.
 constexpr int kSplitKWaves = 8;   // waves per workgroup (two per SIMD), one workgroup per CU
 constexpr int kSplitKBatch = 4;   // k-steps per batch
 constexpr int kTiledStage = 8;    // k-steps per stage of the tiled kernel (128 of K)
+
+// Decode kernel geometry: one workgroup of kDecodeWaves waves per CU; each
+// wave keeps kDecodePrefetch bodies of weights in flight.
+constexpr int kDecodeWaves = 8;
+constexpr int kDecodePrefetch = 3;
+// LDS budget of the decode kernel (X rows + partial-tile slots), per workgroup,
+// and the 16-byte pieces of X each of its threads copies into LDS (enough for
+// any X within the budget: 16 * 512 * 16 bytes = 128 KiB).
+constexpr size_t kDecodeLdsMax = 160 * 1024;
+constexpr int kDecodeXPieces = 16;
+constexpr size_t kDecodeXMax = (size_t)kDecodeXPieces * kDecodeWaves * 64 * 16;
+
+// LDS bytes of a decode launch: M rows of X (2K bytes + 16 padding each), the
+// [2 items][waves][tiles per item][row groups][64 lanes] fp32x4 partial-tile
+// slots and four counters.
+inline size_t decode_lds_bytes(int64_t M, int64_t K, int tpi, int mb) {
+    return (size_t)M * (size_t)(2 * K + 16) + (size_t)2 * kDecodeWaves * tpi * (mb / 8) * 64 * 16 +
+           16;
+}
 
 // How one w4a16_gemm call is executed.  Computed on the host from the shape
 // only, so w4a16_workspace_bytes and w4a16_gemm always agree.
@@ -29,6 +51,8 @@ struct Plan {
     int waves;             // waves per workgroup
     int grid_x, grid_y, grid_z;
     int tiles;             // output tiles that own a counter (0 if splits == 1)
+    int items;             // decode: items of tpi tiles (32 columns each)
+    int tpi;               // decode: tiles per item
     size_t tile_floats;    // fp32 partial values per (tile, split)
     size_t counters_bytes; // counter area at the start of the workspace
     size_t workspace;      // total workspace bytes (0 if splits == 1)
@@ -89,6 +113,14 @@ w4a16_status_t run_gemm(const GemmCall& c, const void* X, const void* packed, vo
 // Byte size of the counter area at the start of every workspace (the same
 // for every shape).
 constexpr size_t kCounterBytes = 64 * 1024;
+#define W4A16_DECLARE_DECODE_PART(name)                                                       \
+    hipError_t name(const void* X, const void* packed, void* Y, int64_t M, const Layout& L, \
+                    const Plan& plan, const Epilogue& ep, hipStream_t stream);
+W4A16_DECLARE_DECODE_PART(launch_decode_f16)
+W4A16_DECLARE_DECODE_PART(launch_decode_f16_ep)
+W4A16_DECLARE_DECODE_PART(launch_decode_bf16)
+W4A16_DECLARE_DECODE_PART(launch_decode_bf16_ep)
+#undef W4A16_DECLARE_DECODE_PART
 // Read-bandwidth probe geometry: one workgroup of 8 waves per CU.
 constexpr int kProbeBlocks = 256;
 constexpr int kProbeThreads = 512;
