@@ -80,8 +80,7 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int G, uint32_t flags) {
 
     // The decode kernel holds X in LDS: it serves M <= 8 whenever X fits.
     auto decode_fits = [&](int tpi) {
-        return decode_lds_bytes(M, K, tpi, M <= 8 ? 8 : 32) <= kDecodeLdsMax &&
-               (size_t)M * (size_t)K * 2 <= kDecodeXMax;
+        return decode_lds_bytes(M, K, tpi, M <= 8 ? 8 : 32) <= kDecodeLdsMax;
     };
     Variant v;
     if (hint == W4A16_PLAN_DECODE && M <= 32 && decode_fits(1))

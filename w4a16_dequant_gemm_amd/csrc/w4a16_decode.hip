@@ -52,12 +52,6 @@ namespace {
 
 constexpr int DW = kDecodeWaves;   // waves per workgroup
 
-// LDS barrier that waits for this wave's LDS operations only: global loads
-// stay in flight across it (the compiler waits for each where it is used).
-__device__ __forceinline__ void barrier_lds() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
 template <int DT, bool SYM, int G, int MB, int TPI, int PB, bool EP>
 __global__ __launch_bounds__(DW * 64) void decode_kernel(
     const uint16_t* __restrict__ X, const uint8_t* __restrict__ packed, uint16_t* __restrict__ Y,
@@ -68,6 +62,7 @@ __global__ __launch_bounds__(DW * 64) void decode_kernel(
     constexpr int ZE = EPB / 2;              // zero entry bytes
     constexpr int QMAX = MB / 8;             // 8-row accumulator groups that can hold rows < M
     constexpr int R = PB + 1;                // bodies held per wave (ring)
+    constexpr int EARLY = kDecodeEarlyBodies < PB ? kDecodeEarlyBodies : PB;
     extern __shared__ __align__(16) uint8_t lds[];
 
     const int tid = threadIdx.x;
@@ -84,15 +79,15 @@ __global__ __launch_bounds__(DW * 64) void decode_kernel(
     const int nsteps = my_items * nbw;
 
     // LDS: X rows (row stride RS bytes), the partial-tile slots of two
-    // items, their two arrival counters and two counts of reduced items
+    // items, their two arrival counters, two counts of reduced items and the
+    // waves' progress counters
     const int RS = 2 * K + 16;
     f32x4* slots = (f32x4*)(lds + (size_t)M * RS);   // [2][DW][TPI][QMAX][64]
     uint32_t* cnt = (uint32_t*)(slots + 2 * DW * TPI * QMAX * 64);
+    uint32_t* prog = cnt + 4;                        // [DW] bodies computed per wave
     auto slot = [&](int par, int w, int tt, int q) -> f32x4& {
         return slots[(((par * DW + w) * TPI + tt) * QMAX + q) * 64 + lane];
     };
-    if (tid < 4) cnt[tid] = 0u;
-
     const bool exact = [&] {
         if constexpr (DT == DT_F16) {
             return false;
@@ -110,14 +105,13 @@ __global__ __launch_bounds__(DW * 64) void decode_kernel(
     const uint32_t lane16 = (uint32_t)lane * 16;
     const int c32 = lane & 31;
     // issue cursor: item j of this workgroup, body b0 + ib of this wave; past
-    // the last body it stays on the last one (cached, never used).  A wave
-    // without bodies (K below 256 * waves) loads body 0 and never uses it.
-    // Every call issues the same loads, so the compiler counts them exactly.
+    // the last body it stays on the last one (cached, never used).  Every call
+    // issues the same loads, so the compiler counts them exactly.
     int ij = 0, ib = 0;
     auto issue = [&](Bundle& B) {
         const bool real = ij < my_items;
         const int j = real ? ij : my_items - 1;
-        const int b = nbw == 0 ? 0 : b0 + (real ? ib : nbw - 1);
+        const int b = b0 + (real ? ib : nbw - 1);
         const int item = (int)blockIdx.x + j * (int)gridDim.x;
 #pragma unroll
         for (int tt = 0; tt < TPI; ++tt) {
@@ -136,47 +130,72 @@ __global__ __launch_bounds__(DW * 64) void decode_kernel(
         }
     };
 
-    // ---- X into LDS, and the first PB bodies' loads, all issued at once: X
-    // first (16-byte pieces, NP per thread with NP the power of two that
-    // covers X -- at most kDecodeXPieces, the LDS budget bounds X -- loaded
-    // unconditionally at clamped addresses so that the compiler counts
-    // exactly how many loads are outstanding), then the bodies; each piece is
-    // written to LDS as soon as it has arrived, which waits for the X loads
-    // only, not for the bodies behind them.  Pieces past the end were loaded
-    // from the last one and are written back to its place (the same bytes).
+    // ---- X into LDS, and the first PB bodies' loads.  A wave reads X only in
+    // the K range of its own bodies (the same range in every item), so it
+    // stages just that slice of every row: no other wave waits for it and no
+    // workgroup barrier follows (a wave still issuing its loads, which the
+    // memory pipeline throttles at the start, holds nobody back).  The slice's
+    // first pieces (16 bytes, NP per lane, NP the power of two that covers
+    // them, at most 16) are loaded first, then the first EARLY bodies; each
+    // piece is written to LDS as soon as it has arrived, which waits for the
+    // X loads only, not for the bodies behind them.  Loads are unconditional
+    // at clamped addresses so that the compiler counts exactly how many are
+    // outstanding; a piece past the end is the last one again, written back
+    // to its own place.  Slices of more than 16 pieces per lane continue 16 at
+    // a time, then the remaining bodies are issued.
     Bundle ring[R];
-    const int vpr = K / 8;                        // 16-byte pieces per row
-    const int nvec = M * vpr;
+    const int ppr = nbw * (kBodyK / 8);            // pieces per row of this wave's slice
+    const int npc = M * ppr;                       // pieces of the slice
+    const int xk0 = b0 * kBodyK;                   // first k of the slice
+    auto piece_load = [&](int v) {
+        v = min(v, npc - 1);
+        const int row = v / ppr;
+        return *(const u32x4*)(X + (size_t)row * K + xk0 + (v - row * ppr) * 8);
+    };
+    auto piece_store = [&](int v, const u32x4& x) {
+        v = min(v, npc - 1);
+        const int row = v / ppr;
+        *(u32x4*)(lds + (size_t)row * RS + (size_t)(xk0 + (v - row * ppr) * 8) * 2) = x;
+    };
     auto stage = [&](auto np_) {
         constexpr int NP = decltype(np_)::value;
         u32x4 xv[NP];
 #pragma unroll
-        for (int i = 0; i < NP; ++i)
-            xv[i] = *(const u32x4*)(X + (size_t)min(i * DW * 64 + tid, nvec - 1) * 8);
-        __builtin_amdgcn_sched_barrier(0);   // all X loads, then all body loads
+        for (int i = 0; i < NP; ++i) xv[i] = piece_load(i * 64 + lane);
+        __builtin_amdgcn_sched_barrier(0);   // the X loads, then the early body loads
 #pragma unroll
-        for (int i = 0; i < PB; ++i) issue(ring[i]);
+        for (int i = 0; i < EARLY; ++i) issue(ring[i]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < NP; ++i) {
-            const int v = min(i * DW * 64 + tid, nvec - 1);
-            const int row = v / vpr;
-            *(u32x4*)(lds + (size_t)row * RS + (v - row * vpr) * 16) = xv[i];
+        for (int i = 0; i < NP; ++i) piece_store(i * 64 + lane, xv[i]);
+        __builtin_amdgcn_sched_barrier(0);
+        for (int v0 = NP * 64; v0 < npc; v0 += 16 * 64) {
+            u32x4 xr[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) xr[i] = piece_load(v0 + i * 64 + lane);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) piece_store(v0 + i * 64 + lane, xr[i]);
         }
+        if constexpr (kDecodeRamp) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+#pragma unroll
+        for (int i = EARLY; i < PB; ++i) issue(ring[i]);
     };
-    static_assert(kDecodeXPieces == 16, "the piece counts below");
-    const int np = (nvec + DW * 64 - 1) / (DW * 64);
-    if (np <= 1)
+    // counters zeroed before any wave can reach an item end; no global load
+    // has been issued yet, so this barrier costs only the waves' start skew
+    if (tid < 4 + DW) cnt[tid] = 0u;
+    __syncthreads();
+    if (nbw == 0) return;                          // fewer bodies than waves: no work
+    const int npl = (npc + 63) / 64;               // pieces per lane
+    if (npl <= 1)
         stage(std::integral_constant<int, 1>{});
-    else if (np <= 2)
+    else if (npl <= 2)
         stage(std::integral_constant<int, 2>{});
-    else if (np <= 4)
+    else if (npl <= 4)
         stage(std::integral_constant<int, 4>{});
-    else if (np <= 8)
+    else if (npl <= 8)
         stage(std::integral_constant<int, 8>{});
     else
         stage(std::integral_constant<int, 16>{});
-    barrier_lds();
 
     // NACC accumulators per tile (k-steps alternate between them), so that
     // consecutive MFMAs do not wait for each other's result: two for a single
@@ -291,8 +310,27 @@ __global__ __launch_bounds__(DW * 64) void decode_kernel(
         }
     };
 
+    // Waves w and w + 4 share a SIMD, whose issue arbiter favours the older
+    // wave when both are ready; left alone the older one runs ahead and
+    // finishes first, and the other then runs without a partner to overlap
+    // with.  So each wave publishes how many bodies it has computed and takes
+    // the lower priority while it is ahead of its partner (a finished wave
+    // reports "infinitely far", never holding its partner back).
+    auto balance = [&](int done) {
+        if constexpr (kDecodeBalance) {
+            if (lane == 0)
+                __hip_atomic_store(&prog[wave], (uint32_t)done, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+            const uint32_t partner = __builtin_amdgcn_readfirstlane(__hip_atomic_load(
+                &prog[wave ^ (DW / 2)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+            if ((uint32_t)done > partner)
+                __builtin_amdgcn_s_setprio(0);
+            else
+                __builtin_amdgcn_s_setprio(1);
+        }
+    };
+
     auto mainloop = [&](auto ex) {
-        if (nbw == 0) return;                     // fewer bodies than waves: nothing to do
         int j = 0, bb = 0;                        // item and body of step st
         for (int st = 0; st < nsteps; st += R) {
 #pragma unroll
@@ -300,6 +338,7 @@ __global__ __launch_bounds__(DW * 64) void decode_kernel(
                 issue(ring[(r + PB) % R]);
                 if (st + r < nsteps) {
                     compute(ring[r], b0 + bb, ex);
+                    balance(st + r + 1);
                     if (++bb == nbw) {
                         item_end(j);
                         bb = 0;
@@ -307,6 +346,12 @@ __global__ __launch_bounds__(DW * 64) void decode_kernel(
                     }
                 }
             }
+        }
+        if constexpr (kDecodeBalance) {
+            if (lane == 0)
+                __hip_atomic_store(&prog[wave], 0xFFFFFFFFu, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+            __builtin_amdgcn_s_setprio(0);
         }
     };
     if (exact)

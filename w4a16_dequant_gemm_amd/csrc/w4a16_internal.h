@@ -21,22 +21,25 @@ constexpr int kSplitKBatch = 4;   // k-steps per batch
 constexpr int kTiledStage = 8;    // k-steps per stage of the tiled kernel (128 of K)
 
 // Decode kernel geometry: one workgroup of kDecodeWaves waves per CU; each
-// wave keeps kDecodePrefetch bodies of weights in flight.
+// wave keeps kDecodePrefetch bodies of weights in flight, of which the first
+// kDecodeEarlyBodies are issued before the activations are written to LDS
+// (the rest right after).
 constexpr int kDecodeWaves = 8;
 constexpr int kDecodePrefetch = 3;
-// LDS budget of the decode kernel (X rows + partial-tile slots), per workgroup,
-// and the 16-byte pieces of X each of its threads copies into LDS (enough for
-// any X within the budget: 16 * 512 * 16 bytes = 128 KiB).
+constexpr int kDecodeEarlyBodies = 3;
+// Ramp: a wave waits for X and its early bodies before issuing the rest.
+constexpr bool kDecodeRamp = false;
+// Balance: the two waves of a SIMD keep equal progress (wave priorities).
+constexpr bool kDecodeBalance = true;
+// LDS budget of the decode kernel (X rows + partial-tile slots), per workgroup.
 constexpr size_t kDecodeLdsMax = 160 * 1024;
-constexpr int kDecodeXPieces = 16;
-constexpr size_t kDecodeXMax = (size_t)kDecodeXPieces * kDecodeWaves * 64 * 16;
 
 // LDS bytes of a decode launch: M rows of X (2K bytes + 16 padding each), the
 // [2 items][waves][tiles per item][row groups][64 lanes] fp32x4 partial-tile
-// slots and four counters.
+// slots, four counters and one progress counter per wave.
 inline size_t decode_lds_bytes(int64_t M, int64_t K, int tpi, int mb) {
     return (size_t)M * (size_t)(2 * K + 16) + (size_t)2 * kDecodeWaves * tpi * (mb / 8) * 64 * 16 +
-           16;
+           16 + 4 * kDecodeWaves;
 }
 
 // How one w4a16_gemm call is executed.  Computed on the host from the shape
