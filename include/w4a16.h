@@ -63,11 +63,10 @@ typedef enum {
  * benchmarks and tests.  Give the same flags to w4a16_workspace_bytes and to
  * the GEMM call.  A hint that does not apply to the shape is ignored (the
  * default choice is made).  W4A16_PLAN_PARAM(n), n in 1..255, sets the
- * variant's parameter: the decode kernel's workgroup count (at most one per
- * output tile), split-K workgroups in units of 8, or the tiled kernel's split
- * count.
+ * variant's parameter: the decode kernel's workgroup count, split-K
+ * workgroups in units of 8, or the tiled kernel's split count.
  */
-#define W4A16_PLAN_DECODE 0x10u   /* small-M streaming kernel, X held in LDS */
+#define W4A16_PLAN_DECODE 0x10u   /* streaming kernel for M <= 8, X held in LDS */
 #define W4A16_PLAN_SPLITK 0x20u   /* split-K streaming kernel (M <= 32) */
 #define W4A16_PLAN_TILED  0x30u   /* LDS-tiled MFMA kernel */
 #define W4A16_PLAN_MASK   0x30u
@@ -151,7 +150,9 @@ size_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int group_size, ui
  * Kernel choice (W4A16_PLAN_* hints override it): M <= 8 whose activations
  * fit in LDS (M*(2K+16) bytes plus a few KiB, up to 160 KiB) uses the decode
  * kernel (each workgroup streams whole 32-column tiles over all of K, its
- * waves splitting K, no workspace); other M <= 32 use a split-K streaming
+ * waves splitting K; when the tiles do not divide evenly over the
+ * workgroups, the left-over tiles are split along K and their parts meet in
+ * the workspace); other M <= 32 use a split-K streaming
  * kernel (every wave streams an equal contiguous share of the weight chunks;
  * partial sums of a split column block are reduced in a fixed order);
  * larger M uses an LDS-tiled MFMA kernel.  All reduce in a fixed order, so

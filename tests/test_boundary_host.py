@@ -80,16 +80,23 @@ def test_workspace_bytes(lib):
 
 def test_plan_hints(lib):
     """Plan hints are accepted where a plan is made (workspace size, GEMM) and
-    nowhere else; the decode kernel needs no workspace; a hint that does not
-    apply to the shape falls back to the default choice."""
+    nowhere else; the decode kernel needs a workspace only when the tiles do
+    not divide evenly over the workgroups (the left-over tiles are split along
+    K); a hint that does not apply to the shape falls back to the default
+    choice."""
     f = w4.W4A16_FP16
     assert w4.plan_flags(None) == 0
     assert w4.plan_flags("decode") == 0x10 and w4.plan_flags(("splitk", 3)) == 0x320
     for bad in ("fast", ("tiled", 256), ("decode", -1)):
         with pytest.raises(ValueError):
             w4.plan_flags(bad)
-    assert w4.w4a16_workspace_bytes(4, 28672, 8192, 128, f | w4.plan_flags("decode")) == 0
-    assert w4.w4a16_workspace_bytes(4, 28672, 8192, 128, f) == 0          # decode by default
+    # 256 tiles of 32 columns over 256 workgroups: nothing to split
+    assert w4.w4a16_workspace_bytes(4, 8192, 8192, 128, f | w4.plan_flags("decode")) == 0
+    assert w4.w4a16_workspace_bytes(4, 8192, 8192, 128, f) == 0           # decode by default
+    # 896 tiles: 3 rounds, then 128 tiles in two halves of K each: one counter
+    # area plus 2 x 128 partial tiles of 8 rows x 32 columns (fp32)
+    assert w4.w4a16_workspace_bytes(4, 28672, 8192, 128, f) == 65536 + 2 * 128 * 1024
+    assert w4.w4a16_workspace_bytes(4, 28672, 8192, 128, f | w4.plan_flags(("decode", 224))) == 0
     assert w4.w4a16_workspace_bytes(4, 4096, 8192, 128, f | w4.plan_flags(("tiled", 4))) > 0
     # decode holds X in LDS: M = 8 rows of K = 16384 do not fit, the hint is ignored
     assert w4.w4a16_workspace_bytes(8, 4096, 1 << 14, 128, f | w4.plan_flags("decode")) == \

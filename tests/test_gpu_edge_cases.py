@@ -32,7 +32,7 @@ def _gpu():
 CASES = [
     ("decode", 1, 2048, 512, 128),
     (("decode", 2), 8, 1024, 384, 64),
-    (("decode", 4), 24, 1024, 256, 32),
+    (("decode", 3), 7, 1024, 256, 32),
     ("splitk", 1, 2048, 512, 128),
     (("splitk", 3), 7, 1024, 256, 64),
     (("splitk", 2), 30, 1024, 384, 32),

@@ -31,7 +31,7 @@ def _gpu():
 PATHS = [
     ("decode-m1", 1, 2048, 512, 128, "decode"),
     ("decode-m8-one-wg", 8, 1024, 768, 64, ("decode", 1)),
-    ("decode-m20", 20, 1024, 384, 32, ("decode", 5)),
+    ("decode-m7-split", 7, 1024, 384, 32, ("decode", 5)),
     ("splitk-whole-blocks", 3, 2048, 512, 128, "splitk"),
     ("splitk-shared-blocks", 5, 1024, 256, 64, ("splitk", 3)),
     ("splitk-m32", 32, 1024, 384, 32, ("splitk", 2)),

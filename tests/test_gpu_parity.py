@@ -140,7 +140,7 @@ def one_hot_rows(M, K, dtype):
     return X, ks
 
 
-@pytest.mark.parametrize("variant,M", [("decode", 1), ("decode", 8), ("decode", 32),
+@pytest.mark.parametrize("variant,M", [("decode", 1), ("decode", 8), ("decode", 5),
                                        ("splitk", 1), ("splitk", 7), ("splitk", 32),
                                        ("tiled", 20), ("tiled", 64), ("tiled", 130)])
 @pytest.mark.parametrize("K,N,G,dtype,sym", [(512, 384, 128, "fp16", False),
@@ -202,7 +202,7 @@ def test_gemm_matches_oracle(M, K, N, G, dtype, sym):
 
 
 @pytest.mark.parametrize("variant,M,param", [("decode", 1, 1), ("decode", 5, 3), ("decode", 8, 7),
-                                             ("decode", 20, 2), ("decode", 32, 255),
+                                             ("decode", 6, 2), ("decode", 2, 255), ("decode", 3, 16),
                                              ("splitk", 4, 1), ("splitk", 4, 3), ("splitk", 30, 16),
                                              ("splitk", 1, 7), ("splitk", 9, 100), ("splitk", 2, 255),
                                              ("tiled", 8, 1), ("tiled", 32, 2), ("tiled", 96, 5),
@@ -210,8 +210,10 @@ def test_gemm_matches_oracle(M, K, N, G, dtype, sym):
 def test_gemm_forced_variant_and_param(variant, M, param):
     """Forced kernel and work split.  decode: `param` workgroups share the 20
     output tiles (1 = one workgroup runs every item in turn, so the item slots
-    are reused many times); split-K: 8*param workgroups (2040 = more than
-    there are batches); tiled: `param` K-splits."""
+    are reused many times; 3, 7, 16: left-over tiles split along K in two
+    halves, the split items first; 255: every tile in two halves); split-K:
+    8*param workgroups (2040 = more than there are batches); tiled: `param`
+    K-splits."""
     K, N, G = 4096, 640, 64
     p = synth.make_problem(M, K, N, G=G, dtype="bf16", sym=False, seed=M)
     say(f"forced {variant} param={param} M={M}")
@@ -239,7 +241,7 @@ def test_workspace_counters_return_to_zero():
         p = synth.make_problem(M, K, N, G=128, seed=i)
         say(f"workspace reuse call {i}: M={M} K={K} N={N} {var}")
         need = w4.w4a16_workspace_bytes(M, N, K, 128, w4.plan_flags(var))
-        assert (need == 0) == (var == "decode")      # the decode kernel needs none
+        assert need > 0
         d = OnDevice(p)
         Y = w4.w4a16_gemm(d.X, d.packed, workspace=ws, plan=var)
         torch.cuda.synchronize()

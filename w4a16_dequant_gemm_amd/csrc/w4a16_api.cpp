@@ -80,16 +80,16 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int G, uint32_t flags) {
 
     // The decode kernel holds X in LDS: it serves M <= 8 whenever X fits.
     auto decode_fits = [&](int tpi) {
-        return decode_lds_bytes(M, K, tpi, M <= 8 ? 8 : 32) <= kDecodeLdsMax;
+        return M <= kDecodeMaxRows && decode_lds_bytes(M, K, tpi, kDecodeMaxRows) <= kDecodeLdsMax;
     };
     Variant v;
-    if (hint == W4A16_PLAN_DECODE && M <= 32 && decode_fits(1))
+    if (hint == W4A16_PLAN_DECODE && decode_fits(1))
         v = VARIANT_DECODE;
     else if (hint == W4A16_PLAN_SPLITK && M <= 32)
         v = VARIANT_SPLITK;
     else if (hint == W4A16_PLAN_TILED)
         v = VARIANT_TILED;
-    else if (M <= 8 && decode_fits(1))
+    else if (decode_fits(1))
         v = VARIANT_DECODE;
     else if (M <= 32)
         v = VARIANT_SPLITK;
@@ -97,18 +97,27 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int G, uint32_t flags) {
         v = VARIANT_TILED;
 
     if (v == VARIANT_DECODE) {
-        // Items of one tile over all of K, dealt round-robin to one workgroup
-        // per CU; no workspace.
+        // Items of one tile over all of K, one workgroup per CU (or the forced
+        // count).  F = items / W whole rounds are dealt round-robin; the R =
+        // items % W left over are split along K into S = W / R parts (at most
+        // KB / 8, so that every wave has a body of each part, and at most 8),
+        // one per workgroup, so that every workgroup gets the same share.
+        // Split parts meet in the workspace (one counter per split item).
         p.variant = VARIANT_DECODE;
         p.tpi = 1;
         p.items = (int)NT;
         p.waves = kDecodeWaves;
-        p.grid_x = (int)std::min<int64_t>(p.items, cus);
-        if (hint == W4A16_PLAN_DECODE && param > 0)   // forced workgroup count
-            p.grid_x = (int)std::min<int64_t>(p.items, param);
+        int64_t W = cus;
+        if (hint == W4A16_PLAN_DECODE && param > 0) W = param;   // forced workgroup count
+        const int64_t F = NT / W, R = NT % W;
+        int64_t S = R > 0 ? std::min<int64_t>({W / R, K / kBodyK / kDecodeWaves, 8}) : 1;
+        if (S < 2 || R > kMaxTilesSplit) S = 1;
+        p.grid_x = (int)(S > 1 ? (F > 0 ? W : R * S) : std::min<int64_t>(NT, W));
         p.grid_y = 1;
         p.grid_z = 1;
-        p.splits = 1;
+        p.splits = (int)S;
+        p.tiles = S > 1 ? (int)R : 0;
+        p.tile_floats = (size_t)64 * 4;   // one part: 8 rows x 32 columns (64 lanes x 4)
     } else if (v == VARIANT_SPLITK) {
         // Balanced contiguous ranges of batches for every wave of one
         // workgroup per CU (fewer workgroups when there are fewer batches).
@@ -200,10 +209,10 @@ hipError_t launch_gemm(const void* X, const void* packed, void* Y, int64_t M, co
                        hipStream_t stream) {
     if (plan.variant == VARIANT_DECODE) {
         if (bf16)
-            return ep.any ? launch_decode_bf16_ep(X, packed, Y, M, L, plan, ep, stream)
-                          : launch_decode_bf16(X, packed, Y, M, L, plan, ep, stream);
-        return ep.any ? launch_decode_f16_ep(X, packed, Y, M, L, plan, ep, stream)
-                      : launch_decode_f16(X, packed, Y, M, L, plan, ep, stream);
+            return ep.any ? launch_decode_bf16_ep(X, packed, Y, M, L, plan, workspace, ep, stream)
+                          : launch_decode_bf16(X, packed, Y, M, L, plan, workspace, ep, stream);
+        return ep.any ? launch_decode_f16_ep(X, packed, Y, M, L, plan, workspace, ep, stream)
+                      : launch_decode_f16(X, packed, Y, M, L, plan, workspace, ep, stream);
     }
     if (bf16)
         return ep.any ? launch_gemm_bf16_ep(X, packed, Y, M, L, plan, workspace, ep, stream)

@@ -55,7 +55,8 @@ constexpr int DW = kDecodeWaves;   // waves per workgroup
 template <int DT, bool SYM, int G, int MB, int TPI, int PB, bool EP>
 __global__ __launch_bounds__(DW * 64) void decode_kernel(
     const uint16_t* __restrict__ X, const uint8_t* __restrict__ packed, uint16_t* __restrict__ Y,
-    int M, int N, int K, int n_items, size_t s_off, size_t z_off, size_t t_off, Epilogue ep) {
+    int M, int N, int K, int n_items, int tail_items, int tail_parts, uint8_t* __restrict__ ws,
+    size_t s_off, size_t z_off, size_t t_off, Epilogue ep) {
     constexpr int EPB = kBodyK / G;          // groups per body: 2, 4, 8
     constexpr int GS = G / kKStep;           // k-steps per group: 8, 4, 2
     constexpr int SE = 2 * EPB;              // scale entry bytes
@@ -63,6 +64,17 @@ __global__ __launch_bounds__(DW * 64) void decode_kernel(
     constexpr int QMAX = MB / 8;             // 8-row accumulator groups that can hold rows < M
     constexpr int R = PB + 1;                // bodies held per wave (ring)
     constexpr int EARLY = kDecodeEarlyBodies < PB ? kDecodeEarlyBodies : PB;
+    // Scale after the product (fp16, at most 8 rows): each group's MFMAs
+    // multiply X by the exact (q - z) into a temporary accumulator t, then
+    // the rows that can hold outputs (registers 0..3: rows 0..7) take
+    // acc += s * t, one fp32 fma per row instead of a v_pk_mul_f16 per
+    // weight pair.  t's registers 0..3 are zeroed at the start of each group
+    // (the other twelve only ever feed rows 8..31, which are never read; they
+    // start at zero and stay finite).  The sum differs from the dequantized-weight product
+    // only by the rounding of each weight to fp16 (at most 2^-11 of each
+    // term), and stays exact where the pages' result is: q = z gives products
+    // of exact zeros, a one-hot row gives s * (q - z) rounded once.
+    constexpr bool SA = kDecodeScaleAfter && DT == DT_F16 && MB == 8 && TPI == 1;
     extern __shared__ __align__(16) uint8_t lds[];
 
     const int tid = threadIdx.x;
@@ -75,8 +87,29 @@ __global__ __launch_bounds__(DW * 64) void decode_kernel(
     const int bbase = KB / DW, brem = KB % DW;
     const int b0 = wave * bbase + min(wave, brem);
     const int nbw = bbase + (wave < brem ? 1 : 0);
-    const int my_items = (n_items - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
-    const int nsteps = my_items * nbw;
+    // This workgroup's items.  Without a tail split (tail_parts == 1) it runs
+    // items g, g + W, g + 2W, ... (W workgroups).  With one (S = tail_parts
+    // > 1) the last tail_items items are split along K into S parts, so that
+    // every workgroup gets the same share of the work: workgroup g <
+    // tail_items * S first runs part g % S of item F*W + g / S, then the full
+    // items g, g + W, ..., g + (F-1)*W, F = (n_items - tail_items) / W.  Part
+    // p of an item is, in every wave, the bodies b0 + p, b0 + p + S, ... of
+    // the wave's own range (the plan keeps S <= KB / 8, so each wave has at
+    // least one), so X is staged once for both kinds of item.
+    const int W = (int)gridDim.x, g = (int)blockIdx.x;
+    const int S = tail_parts;
+    const int F = S > 1 ? (n_items - tail_items) / W : (n_items - g + W - 1) / W;
+    const bool has_tail = S > 1 && g < tail_items * S;
+    const int tail_idx = S > 1 ? g / S : 0;          // index among the split items
+    const int tail_item = F * W + tail_idx;
+    const int tp = g - tail_idx * S;                 // part
+    const int ntb = has_tail ? (nbw - tp + S - 1) / S : 0;
+    const int n_seq = F + (has_tail ? 1 : 0);        // items in this workgroup's sequence
+    const int nsteps = ntb + F * nbw;
+    auto is_tail = [&](int j) { return has_tail && j == 0; };
+    auto item_of = [&](int j) { return is_tail(j) ? tail_item : (j - (has_tail ? 1 : 0)) * W + g; };
+    auto body_of = [&](int j, int i) { return is_tail(j) ? b0 + tp + i * S : b0 + i; };
+    auto len_of = [&](int j) { return is_tail(j) ? ntb : nbw; };
 
     // LDS: X rows (row stride RS bytes), the partial-tile slots of two
     // items, their two arrival counters, two counts of reduced items and the
@@ -104,15 +137,15 @@ __global__ __launch_bounds__(DW * 64) void decode_kernel(
     };
     const uint32_t lane16 = (uint32_t)lane * 16;
     const int c32 = lane & 31;
-    // issue cursor: item j of this workgroup, body b0 + ib of this wave; past
-    // the last body it stays on the last one (cached, never used).  Every call
-    // issues the same loads, so the compiler counts them exactly.
+    // issue cursor: item j of this workgroup's sequence, its body ib of this
+    // wave; past the last body it stays on the last one (cached, never used).
+    // Every call issues the same loads, so the compiler counts them exactly.
     int ij = 0, ib = 0;
     auto issue = [&](Bundle& B) {
-        const bool real = ij < my_items;
-        const int j = real ? ij : my_items - 1;
-        const int b = b0 + (real ? ib : nbw - 1);
-        const int item = (int)blockIdx.x + j * (int)gridDim.x;
+        const bool real = ij < n_seq;
+        const int j = real ? ij : n_seq - 1;
+        const int b = body_of(j, real ? ib : len_of(j) - 1);
+        const int item = item_of(j);
 #pragma unroll
         for (int tt = 0; tt < TPI; ++tt) {
             const int t = item * TPI + tt;
@@ -124,7 +157,7 @@ __global__ __launch_bounds__(DW * 64) void decode_kernel(
             B.s[tt] = load_sent<G>(packed + s_off + ent * SE);
             B.z[tt] = SYM ? 0u : load_zent<G>(packed + z_off + ent * ZE);
         }
-        if (++ib >= nbw) {
+        if (++ib >= len_of(ij)) {
             ib = 0;
             ++ij;
         }
@@ -206,6 +239,8 @@ __global__ __launch_bounds__(DW * 64) void decode_kernel(
     for (int tt = 0; tt < TPI; ++tt)
 #pragma unroll
         for (int h = 0; h < NACC; ++h) acc[tt][h] = f32x16{};
+    f32x4 acc_sa = f32x4{};                      // scale-after: rows 0..7 of the tile
+    f32x16 t_sa = f32x16{};                      // scale-after: one group's product
 
     const Magic mg = make_magic();
     const uint32_t zsh = zent_shift<G>(c32);   // this lane's zero entry in its dword
@@ -220,6 +255,37 @@ __global__ __launch_bounds__(DW * 64) void decode_kernel(
 #pragma unroll
         for (int kk = 0; kk < 16; ++kk) a[kk] = *(const u32x4*)(abase + kk * (kKStep * 2));
         __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the body's work
+        if constexpr (SA) {
+            uint32_t bA = 0, bB = 0;
+            float sc = 0.f;
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int kk = 4 * cc + u;        // k-step inside the body
+                    if (kk % GS == 0) {
+                        const int e = kk / GS;
+                        const uint32_t sword = B.s[0].word(e >> 1);
+                        const uint32_t sbits = (e & 1) ? (sword >> 16) : (sword & 0xFFFFu);
+                        const uint32_t z = SYM ? 8u : (((B.z[0] >> zsh) >> (4 * e)) & 0xFu);
+                        bA = (0x6400u | z) * 0x00010001u;            // fp16 1024 + z
+                        bB = (0x5400u | (z << 4)) * 0x00010001u;     // fp16 64 + z
+                        sc = (float)__builtin_bit_cast(_Float16, (uint16_t)sbits);
+                    }
+                    const u32x4 bop = unpack_qz(B.w[0][cc][u], bA, bB, mg);
+                    if (kk % GS == 0) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) t_sa[r] = opaque_f(0.f);
+                    }
+                    t_sa = mfma32x32x16<DT>(a[kk], bop, t_sa);
+                    if (kk % GS == GS - 1) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) acc_sa[r] = __builtin_fmaf(sc, t_sa[r], acc_sa[r]);
+                    }
+                }
+            }
+            return;
+        }
         ColParams<DT> prm[TPI];
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
@@ -239,6 +305,62 @@ __global__ __launch_bounds__(DW * 64) void decode_kernel(
                 }
             }
         }
+    };
+
+    // Part tp of a split item, summed over this workgroup's waves (v), meets
+    // the other S - 1 parts, each from another workgroup.  Every part is
+    // stored to its slot in the workspace with device-scope stores (sc1: they
+    // write through the per-XCD L2, which is not coherent between XCDs); the
+    // wave waits until its stores have completed (vmcnt(0)) and only then
+    // bumps the item's counter with a device-scope atomic.  The workgroup
+    // whose atomic returns S - 1 is the last: every other part's stores
+    // completed before that part's atomic, which came before this one, so its
+    // device-scope loads (which bypass the L2 as well) read them.  It adds
+    // the S parts in part order 0..S-1 (its own from registers, the same
+    // values it stored: bitwise reproducible), resets the counter for the
+    // next call and stores Y.  Nobody waits for anybody.  The tail part is
+    // the first item of the workgroup, so these round trips overlap the full
+    // items that follow.  Returns true in the last workgroup.
+    const uint32_t part_bytes = (uint32_t)(TPI * QMAX * 64 * 16);
+    auto tail_exchange = [&](f32x4 (&v)[TPI][QMAX]) -> bool {
+        uint32_t* wcnt = (uint32_t*)ws + tail_idx;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            ws + kCounterBytes + (size_t)tail_idx * S * part_bytes, (short)0, (int)(S * part_bytes),
+            kBufferRsrcWord3);
+        const uint32_t lane_off = (uint32_t)lane * 16;
+        auto off = [&](int part, int tt, int q) {
+            return (int)(part * part_bytes + (tt * QMAX + q) * 1024 + lane_off);
+        };
+#pragma unroll
+        for (int tt = 0; tt < TPI; ++tt)
+#pragma unroll
+            for (int q = 0; q < QMAX; ++q)
+                if (q < QM)
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v[tt][q]), rs,
+                                                           off(tp, tt, q), 0, kDeviceScope);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        uint32_t old = 0;
+        if (lane == 0)
+            old = __hip_atomic_fetch_add(wcnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        old = __builtin_amdgcn_readfirstlane(old);
+        asm volatile("" ::: "memory");
+        if ((int)old != S - 1) return false;
+#pragma unroll
+        for (int tt = 0; tt < TPI; ++tt)
+#pragma unroll
+            for (int q = 0; q < QMAX; ++q) {
+                if (q >= QM) continue;
+                f32x4 sum = tp == 0 ? v[tt][q]
+                                    : __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                    rs, off(0, tt, q), 0, kDeviceScope));
+                for (int sp = 1; sp < S; ++sp)
+                    sum += sp == tp ? v[tt][q]
+                                    : __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                    rs, off(sp, tt, q), 0, kDeviceScope));
+                v[tt][q] = sum;
+            }
+        if (lane == 0) __hip_atomic_store(wcnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return true;
     };
 
     // End of item j (the j-th of this workgroup), without a barrier: each wave
@@ -263,23 +385,28 @@ __global__ __launch_bounds__(DW * 64) void decode_kernel(
                 __builtin_amdgcn_s_sleep(1);
             }
         }
+        if constexpr (SA) {
+            slot(par, wave, 0, 0) = acc_sa;
+            acc_sa = f32x4{};
+        } else {
 #pragma unroll
-        for (int tt = 0; tt < TPI; ++tt)
+            for (int tt = 0; tt < TPI; ++tt)
 #pragma unroll
-            for (int q = 0; q < QMAX; ++q)
-                if (q < QM) {
-                    f32x4 v = f32x4{acc[tt][0][4 * q], acc[tt][0][4 * q + 1], acc[tt][0][4 * q + 2],
-                                    acc[tt][0][4 * q + 3]};
+                for (int q = 0; q < QMAX; ++q)
+                    if (q < QM) {
+                        f32x4 v = f32x4{acc[tt][0][4 * q], acc[tt][0][4 * q + 1],
+                                        acc[tt][0][4 * q + 2], acc[tt][0][4 * q + 3]};
 #pragma unroll
-                    for (int h = 1; h < NACC; ++h)
-                        v += f32x4{acc[tt][h][4 * q], acc[tt][h][4 * q + 1], acc[tt][h][4 * q + 2],
-                                   acc[tt][h][4 * q + 3]};
-                    slot(par, wave, tt, q) = v;
-                }
+                        for (int h = 1; h < NACC; ++h)
+                            v += f32x4{acc[tt][h][4 * q], acc[tt][h][4 * q + 1],
+                                       acc[tt][h][4 * q + 2], acc[tt][h][4 * q + 3]};
+                        slot(par, wave, tt, q) = v;
+                    }
 #pragma unroll
-        for (int tt = 0; tt < TPI; ++tt)
+            for (int tt = 0; tt < TPI; ++tt)
 #pragma unroll
-            for (int h = 0; h < NACC; ++h) acc[tt][h] = f32x16{};
+                for (int h = 0; h < NACC; ++h) acc[tt][h] = f32x16{};
+        }
         // the slot writes are complete (LDS only: loads in flight stay in flight)
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         uint32_t old = 0;
@@ -288,26 +415,36 @@ __global__ __launch_bounds__(DW * 64) void decode_kernel(
         old = __builtin_amdgcn_readfirstlane(old);
         asm volatile("" ::: "memory");
         if ((int)old != nact - 1) return;
-        const int item = (int)blockIdx.x + j * (int)gridDim.x;
+        f32x4 v[TPI][QMAX];
 #pragma unroll
         for (int tt = 0; tt < TPI; ++tt)
 #pragma unroll
             for (int q = 0; q < QMAX; ++q) {
                 if (q >= QM) continue;
-                f32x4 v = slot(par, 0, tt, q);
-                for (int w = 1; w < nact; ++w) v += slot(par, w, tt, q);
-                const int64_t col = (int64_t)(item * TPI + tt) * kTileCols + c32;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = 8 * q + 4 * (lane >> 5) + i;
-                    if (row < M) Y[(int64_t)row * N + col] = out_value<DT, EP>(v[i], row, col, N, ep);
-                }
+                v[tt][q] = slot(par, 0, tt, q);
+                for (int w = 1; w < nact; ++w) v[tt][q] += slot(par, w, tt, q);
             }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // slot reads done
+        // the slots are free again once their reads are done
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         if (lane == 0) {
             __hip_atomic_store(&cnt[par], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             __hip_atomic_fetch_add(&cnt[2 + par], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         }
+        if (is_tail(j) && !tail_exchange(v)) return;
+        const int item = item_of(j);
+#pragma unroll
+        for (int tt = 0; tt < TPI; ++tt)
+#pragma unroll
+            for (int q = 0; q < QMAX; ++q) {
+                if (q >= QM) continue;
+                const int64_t col = (int64_t)(item * TPI + tt) * kTileCols + c32;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 8 * q + 4 * (lane >> 5) + i;
+                    if (row < M)
+                        Y[(int64_t)row * N + col] = out_value<DT, EP>(v[tt][q][i], row, col, N, ep);
+                }
+            }
     };
 
     // Waves w and w + 4 share a SIMD, whose issue arbiter favours the older
@@ -337,9 +474,9 @@ __global__ __launch_bounds__(DW * 64) void decode_kernel(
             for (int r = 0; r < R; ++r) {
                 issue(ring[(r + PB) % R]);
                 if (st + r < nsteps) {
-                    compute(ring[r], b0 + bb, ex);
+                    compute(ring[r], body_of(j, bb), ex);
                     balance(st + r + 1);
-                    if (++bb == nbw) {
+                    if (++bb == len_of(j)) {
                         item_end(j);
                         bb = 0;
                         ++j;
@@ -362,33 +499,35 @@ __global__ __launch_bounds__(DW * 64) void decode_kernel(
 
 template <int DT, bool SYM, int G, int MB, int TPI, int PB>
 hipError_t launch_decode_t(const void* X, const void* packed, void* Y, int64_t M,
-                           const Layout& L, const Plan& p, const Epilogue& ep,
+                           const Layout& L, const Plan& p, void* workspace, const Epilogue& ep,
                            hipStream_t stream) {
     constexpr bool EPF = W4A16_TU_EP != 0;
     const size_t lds = decode_lds_bytes(M, L.K, TPI, MB);
     auto kern = decode_kernel<DT, SYM, G, MB, TPI, PB, EPF>;
     hipLaunchKernelGGL(kern, dim3(p.grid_x), dim3(DW * 64), lds, stream, (const uint16_t*)X,
                        (const uint8_t*)packed, (uint16_t*)Y, (int)M, (int)L.N, (int)L.K,
-                       p.items, L.s_off, L.z_off, L.t_off, ep);
+                       p.items, p.tiles, p.splits, (uint8_t*)workspace, L.s_off, L.z_off, L.t_off,
+                       ep);
     return hipGetLastError();
 }
 
 template <int DT, bool SYM, int G>
 hipError_t launch_decode_g(const void* X, const void* packed, void* Y, int64_t M,
-                           const Layout& L, const Plan& p, const Epilogue& ep,
+                           const Layout& L, const Plan& p, void* workspace, const Epilogue& ep,
                            hipStream_t stream) {
     constexpr int PB = kDecodePrefetch;
-    if (M <= 8) return launch_decode_t<DT, SYM, G, 8, 1, PB>(X, packed, Y, M, L, p, ep, stream);
-    return launch_decode_t<DT, SYM, G, 32, 1, PB>(X, packed, Y, M, L, p, ep, stream);
+    if (M > kDecodeMaxRows) return hipErrorInvalidValue;   // the plan never asks for it
+    return launch_decode_t<DT, SYM, G, kDecodeMaxRows, 1, PB>(X, packed, Y, M, L, p, workspace, ep,
+                                                              stream);
 }
 
 template <int DT, bool SYM>
 hipError_t launch_decode_s(const void* X, const void* packed, void* Y, int64_t M,
-                           const Layout& L, const Plan& p, const Epilogue& ep,
+                           const Layout& L, const Plan& p, void* workspace, const Epilogue& ep,
                            hipStream_t stream) {
-    if (L.G == 128) return launch_decode_g<DT, SYM, 128>(X, packed, Y, M, L, p, ep, stream);
-    if (L.G == 64) return launch_decode_g<DT, SYM, 64>(X, packed, Y, M, L, p, ep, stream);
-    return launch_decode_g<DT, SYM, 32>(X, packed, Y, M, L, p, ep, stream);
+    if (L.G == 128) return launch_decode_g<DT, SYM, 128>(X, packed, Y, M, L, p, workspace, ep, stream);
+    if (L.G == 64) return launch_decode_g<DT, SYM, 64>(X, packed, Y, M, L, p, workspace, ep, stream);
+    return launch_decode_g<DT, SYM, 32>(X, packed, Y, M, L, p, workspace, ep, stream);
 }
 
 }  // namespace
@@ -408,11 +547,11 @@ hipError_t launch_decode_s(const void* X, const void* packed, void* Y, int64_t M
 #endif
 
 hipError_t W4A16_DECODE_ENTRY(const void* X, const void* packed, void* Y, int64_t M,
-                              const Layout& L, const Plan& p, const Epilogue& ep,
+                              const Layout& L, const Plan& p, void* workspace, const Epilogue& ep,
                               hipStream_t stream) {
     constexpr int DT = W4A16_TU_BF16 ? DT_BF16 : DT_F16;
-    if (L.sym) return launch_decode_s<DT, true>(X, packed, Y, M, L, p, ep, stream);
-    return launch_decode_s<DT, false>(X, packed, Y, M, L, p, ep, stream);
+    if (L.sym) return launch_decode_s<DT, true>(X, packed, Y, M, L, p, workspace, ep, stream);
+    return launch_decode_s<DT, false>(X, packed, Y, M, L, p, workspace, ep, stream);
 }
 
 }  // namespace w4a16

@@ -32,6 +32,13 @@
 
 namespace w4a16 {
 
+// Buffer resource word 3 for raw (untyped) buffer accesses, and the cache
+// policy bit of device-scope accesses (sc1: they bypass the per-XCD L2, the
+// same policy the device-scope atomics use), for partial sums exchanged
+// between workgroups.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+constexpr int kDeviceScope = 16;
+
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -93,6 +100,11 @@ __device__ __forceinline__ uint32_t opaque_v(uint32_t v) {
     return v;
 }
 
+__device__ __forceinline__ float opaque_f(float v) {
+    asm("" : "+v"(v));
+    return v;
+}
+
 // (x & m) | g in one VALU instruction.  The backend splits it into v_and +
 // v_or when both constants are literals (gfx9 VOP3 takes no literal and one
 // scalar operand), so it is written out: mask in an SGPR, g in a VGPR.
@@ -133,6 +145,27 @@ __device__ __forceinline__ u32x4 dequant_word(uint32_t w, const ColParams<DT_F16
     r.y = __builtin_bit_cast(uint32_t, (f16x2)((v1 - bB) * s2));
     r.z = __builtin_bit_cast(uint32_t, (f16x2)((v2 - bA) * s2));
     r.w = __builtin_bit_cast(uint32_t, (f16x2)((v3 - bB) * s2));
+    return r;
+}
+
+// (q - z) of the eight weights of one repacked word, exact small integers in
+// fp16, as the four dwords of an MFMA operand (the group scale is applied to
+// the product later).  bA = (1024+z, 1024+z), bB = (64+z, 64+z) as fp16.
+// 9 VALU instructions: 1 shift, 4 v_and_or_b32, 4 v_pk_add_f16.
+__device__ __forceinline__ u32x4 unpack_qz(uint32_t w, uint32_t bA_bits, uint32_t bB_bits,
+                                           const Magic& mg) {
+    const uint32_t w8 = w >> 8;
+    const f16x2 bA = __builtin_bit_cast(f16x2, bA_bits);
+    const f16x2 bB = __builtin_bit_cast(f16x2, bB_bits);
+    const f16x2 v0 = __builtin_bit_cast(f16x2, and_or(w, 0x000F000Fu, mg.a));    // 1024 + q
+    const f16x2 v1 = __builtin_bit_cast(f16x2, and_or(w, 0x00F000F0u, mg.b));    // 64 + q
+    const f16x2 v2 = __builtin_bit_cast(f16x2, and_or(w8, 0x000F000Fu, mg.a));
+    const f16x2 v3 = __builtin_bit_cast(f16x2, and_or(w8, 0x00F000F0u, mg.b));
+    u32x4 r;
+    r.x = __builtin_bit_cast(uint32_t, (f16x2)(v0 - bA));
+    r.y = __builtin_bit_cast(uint32_t, (f16x2)(v1 - bB));
+    r.z = __builtin_bit_cast(uint32_t, (f16x2)(v2 - bA));
+    r.w = __builtin_bit_cast(uint32_t, (f16x2)(v3 - bB));
     return r;
 }
 

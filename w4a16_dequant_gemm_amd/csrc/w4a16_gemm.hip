@@ -113,10 +113,6 @@ __device__ __forceinline__ bool uses_exact_form(const uint8_t* packed, size_t t_
 // A seq_cst __threadfence() here would write back and invalidate a whole
 // XCD's L2 per workgroup, which costs far more than the GEMM itself.
 // ---------------------------------------------------------------------------
-// Buffer resource word 3 for raw (untyped) buffer accesses, and the cache
-// policy bit of device-scope accesses (sc1), as used by the atomics below.
-constexpr int kBufferRsrcWord3 = 0x00020000;
-constexpr int kDeviceScope = 16;
 __device__ __forceinline__ void st_dev(float* p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

@@ -25,12 +25,16 @@ constexpr int kTiledStage = 8;    // k-steps per stage of the tiled kernel (128 
 // kDecodeEarlyBodies are issued before the activations are written to LDS
 // (the rest right after).
 constexpr int kDecodeWaves = 8;
-constexpr int kDecodePrefetch = 3;
+constexpr int kDecodeMaxRows = 8;   // M served by the decode kernel (one 8-row group)
+constexpr int kDecodePrefetch = 1;
 constexpr int kDecodeEarlyBodies = 3;
 // Ramp: a wave waits for X and its early bodies before issuing the rest.
 constexpr bool kDecodeRamp = false;
 // Balance: the two waves of a SIMD keep equal progress (wave priorities).
 constexpr bool kDecodeBalance = true;
+// fp16, M <= 8: the group scale multiplies the MFMA's product of X and the
+// exact (q - z) instead of every weight.
+constexpr bool kDecodeScaleAfter = true;
 // LDS budget of the decode kernel (X rows + partial-tile slots), per workgroup.
 constexpr size_t kDecodeLdsMax = 160 * 1024;
 
@@ -53,7 +57,8 @@ struct Plan {
     int mt;                // 32-row MFMA tiles per wave
     int waves;             // waves per workgroup
     int grid_x, grid_y, grid_z;
-    int tiles;             // output tiles that own a counter (0 if splits == 1)
+    int tiles;             // output tiles that own a counter (0 if splits == 1); decode:
+                           // the items split along K (their parts: splits)
     int items;             // decode: items of tpi tiles (32 columns each)
     int tpi;               // decode: tiles per item
     size_t tile_floats;    // fp32 partial values per (tile, split)
@@ -118,7 +123,7 @@ w4a16_status_t run_gemm(const GemmCall& c, const void* X, const void* packed, vo
 constexpr size_t kCounterBytes = 64 * 1024;
 #define W4A16_DECLARE_DECODE_PART(name)                                                       \
     hipError_t name(const void* X, const void* packed, void* Y, int64_t M, const Layout& L, \
-                    const Plan& plan, const Epilogue& ep, hipStream_t stream);
+                    const Plan& plan, void* workspace, const Epilogue& ep, hipStream_t stream);
 W4A16_DECLARE_DECODE_PART(launch_decode_f16)
 W4A16_DECLARE_DECODE_PART(launch_decode_f16_ep)
 W4A16_DECLARE_DECODE_PART(launch_decode_bf16)
