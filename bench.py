@@ -126,7 +126,12 @@ def cpu_baseline(name, cfg, budget_s=12.0):
     }
 
 
-KERNEL_SOURCES = ("w4a16_gemm.hip", "w4a16_device.h", "w4a16_layout.h", "w4a16_api.cpp")
+KERNEL_SOURCES = ("w4a16_gemm.hip", "w4a16_decode.hip", "w4a16_device.h", "w4a16_epilogue.h",
+                  "w4a16_layout.h", "w4a16_internal.h", "w4a16_api.cpp")
+# Reported beside the headline workload (same protocol, no CPU baseline or
+# comparators): the prefill and the batched shapes of the same layer.
+EXTRA_WORKLOADS = ("prefill_m4096_k8192_n28672_bf16_asym_g128",
+                   "batch_m64_k8192_n28672_fp16_asym_g64")
 
 
 def kernel_source_hash():
@@ -447,6 +452,8 @@ def main():
                          "one of " + ", ".join(LAYER_WORKLOADS) + " (fused FFN block)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-comparators", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the extra workloads reported beside a single workload")
     ap.add_argument("--plan", default=None,
                     help="kernel hint, e.g. decode, decode:2, splitk, tiled:4 (default: the "
                          "library's own choice)")
@@ -479,7 +486,27 @@ def main():
         out = run_workload(name, args.steps, args.warmup,
                            with_cpu=not args.no_cpu and len(names) == 1,
                            comparators=not args.no_comparators, plan=plan)
+        if len(names) == 1 and not args.no_extra and plan is None:
+            out["extra_workloads"] = extra_workloads(name, min(args.steps, 50), min(args.warmup, 5))
         print(json.dumps(out), flush=True)
+
+
+def extra_workloads(headline, steps, warmup):
+    """The roofline entries of EXTRA_WORKLOADS (those other than the headline),
+    measured with the same protocol in the same process."""
+    import torch
+
+    res = {}
+    for name in EXTRA_WORKLOADS:
+        if name == headline:
+            continue
+        o = run_workload(name, steps, warmup, with_cpu=False, comparators=False)
+        res[name] = {k: o[k] for k in ("kernel_us", "ms_per_step", "steps", "roofline",
+                                       "read_probe_gbs", "tflops", "algorithmic_bytes")}
+        res[name]["config"] = {k: o["config"][k] for k in ("M", "K", "N", "group_size",
+                                                           "act_dtype", "quant")}
+        torch.cuda.empty_cache()
+    return res
 
 
 if __name__ == "__main__":

@@ -263,17 +263,26 @@ def workspace_for(nbytes: int, device: torch.device, stream=None) -> Optional[to
     after every call, so the buffer is reused as it is."""
     if nbytes == 0:
         return None
-    key = (device.type, device.index, _stream_handle(stream))
+    index = device.index if device.index is not None else torch.cuda.current_device()
+    return _workspace_at(nbytes, index, _stream_handle(stream))
+
+
+def _workspace_at(nbytes: int, device_index: int, stream_handle: int) -> torch.Tensor:
+    key = (device_index, stream_handle)
     ws = _workspaces.get(key)
-    if ws is None or ws.numel() < nbytes:
-        size = 1 << 20
-        while size < nbytes:
-            size *= 2
-        if ws is not None:
-            _retired_workspaces.append(ws)
-        ws = torch.zeros(size, dtype=torch.uint8, device=device)
-        _workspaces[key] = ws
+    if ws is not None and ws.numel() >= nbytes:
+        return ws
+    size = 1 << 20
+    while size < nbytes:
+        size *= 2
+    if ws is not None:
+        _retired_workspaces.append(ws)
+    ws = torch.zeros(size, dtype=torch.uint8, device=torch.device("cuda", device_index))
+    _workspaces[key] = ws
     return ws
+
+
+_TORCH_DT = {0: torch.float16, W4A16_BF16: torch.bfloat16}
 
 
 def _gemm_args(where, X, packed, M, Y, col_scale=None, bias=None, aux=None, activation="none",
@@ -286,21 +295,23 @@ def _gemm_args(where, X, packed, M, Y, col_scale=None, bias=None, aux=None, acti
     K, N, flags = packed.K, packed.N, packed.flags
     if M is None:
         M = X.shape[0]
-    dt = torch_dtype(flags)
-    _require(X, f"{where}: X", dt, M * K)
-    dev = X.device
-    if packed.data.device != dev:
-        _bad(f"{where}: the blob is on {packed.data.device}, X on {dev}")
+    dt = _TORCH_DT[flags & W4A16_BF16]
+    if (X.dtype != dt or X.numel() != M * K or not X.is_contiguous() or not X.is_cuda):
+        _require(X, f"{where}: X", dt, M * K)     # raises with the details
+    dev_index = X.get_device()
+    if packed.data.get_device() != dev_index:
+        _bad(f"{where}: the blob is on {packed.data.device}, X on {X.device}")
     if Y is None:
-        Y = torch.empty((M, N), dtype=dt, device=dev)
-    else:
-        _require(Y, f"{where}: Y", dt, M * N, dev)
+        Y = torch.empty((M, N), dtype=dt, device=X.device)
+    elif (Y.dtype != dt or Y.numel() != M * N or not Y.is_contiguous() or not Y.is_cuda
+          or Y.get_device() != dev_index):
+        _require(Y, f"{where}: Y", dt, M * N, X.device)
     if col_scale is not None:
-        _require(col_scale, f"{where}: col_scale", torch.float32, N, dev)
+        _require(col_scale, f"{where}: col_scale", torch.float32, N, X.device)
     if bias is not None:
-        _require(bias, f"{where}: bias", dt, N, dev)
+        _require(bias, f"{where}: bias", dt, N, X.device)
     if aux is not None:
-        _require(aux, f"{where}: aux", dt, M * N, dev)
+        _require(aux, f"{where}: aux", dt, M * N, X.device)
     if activation not in W4A16_ACT or aux_op not in W4A16_AUX:
         _bad(f"{where}: activation {activation!r} / aux_op {aux_op!r}")
     ep = None
@@ -317,15 +328,20 @@ def w4a16_gemm(X: torch.Tensor, packed: PackedW4, M: Optional[int] = None,
                stream=None, plan=None) -> torch.Tensor:
     """Y[M][N] = X[M][K] . dequant(packed); X is [M][K] fp16/bf16 on the device.
     `plan`: an optional kernel hint (see plan_flags)."""
-    lib = load_library()
+    lib = _lib if _lib is not None else load_library()
     M, Y, _ = _gemm_args("w4a16_gemm", X, packed, M, Y)
     K, N, G = packed.K, packed.N, packed.group_size
-    flags = packed.flags | plan_flags(plan)
+    flags = packed.flags if plan is None else packed.flags | plan_flags(plan)
+    sh = _stream_handle(stream)
     if workspace is None:
-        workspace = workspace_for(_workspace_need(M, N, K, G, flags), X.device, stream)
-    _check(lib.w4a16_gemm(_ptr(X), _ptr(packed.data), packed.data.numel(), _ptr(Y), M, N, K, G,
-                          flags, _ptr(workspace), 0 if workspace is None else workspace.numel(),
-                          _stream(stream)), "w4a16_gemm")
+        need = _workspace_need(M, N, K, G, flags)
+        if need:
+            workspace = _workspace_at(need, X.get_device(), sh)
+    st = lib.w4a16_gemm(X.data_ptr(), packed.data.data_ptr(), packed.data.numel(), Y.data_ptr(),
+                        M, N, K, G, flags, None if workspace is None else workspace.data_ptr(),
+                        0 if workspace is None else workspace.numel(), sh)
+    if st:
+        _check(st, "w4a16_gemm")
     return Y
 
 
