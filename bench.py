@@ -92,7 +92,7 @@ def cpu_baseline(name, cfg, budget_s=12.0):
                     break
     except OSError:
         pass
-    p = synth.workload(name)
+    p = synth.make_problem(seed=0, **cfg)
     M, K, N, G = cfg["M"], cfg["K"], cfg["N"], cfg["G"]
     rows = min(M, 64)
 
@@ -159,15 +159,17 @@ def measured_traffic(name):
 
 
 def run_workload(name, steps, warmup, rotate_bytes=1 << 30, with_cpu=True, comparators=True,
-                 plan=None):
+                 plan=None, rows=None):
     import torch
 
     import w4a16_dequant_gemm_amd as w4
 
     w4.load_library()
     cfg = dict(synth.WORKLOADS[name])
+    if rows is not None:          # the workload's weights with another number of rows
+        cfg["M"] = rows
     dev = torch.device("cuda:0")
-    p = synth.workload(name)
+    p = synth.make_problem(seed=0, **cfg)
     flags = w4.flags_of(p.dtype, p.sym)
     X, qw, sc, zr = w4.to_device(p, dev)
     base = w4.w4a16_repack(qw, sc, zr, p.K, p.N, p.G, flags)
@@ -452,6 +454,9 @@ def main():
                          "one of " + ", ".join(LAYER_WORKLOADS) + " (fused FFN block)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-comparators", action="store_true")
+    ap.add_argument("--m", type=int, default=None,
+                    help="run the workload's weights with this many activation rows instead "
+                         "(for sweeps of the kernel choice over M)")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the extra workloads reported beside a single workload")
     ap.add_argument("--plan", default=None,
@@ -485,8 +490,8 @@ def main():
     for name in names:
         out = run_workload(name, args.steps, args.warmup,
                            with_cpu=not args.no_cpu and len(names) == 1,
-                           comparators=not args.no_comparators, plan=plan)
-        if len(names) == 1 and not args.no_extra and plan is None:
+                           comparators=not args.no_comparators, plan=plan, rows=args.m)
+        if len(names) == 1 and not args.no_extra and plan is None and args.m is None:
             out["extra_workloads"] = extra_workloads(name, min(args.steps, 50), min(args.warmup, 5))
         print(json.dumps(out), flush=True)
 

@@ -250,15 +250,22 @@ struct SEnt<128> {
     uint32_t v;
     __device__ uint32_t word(int) const { return v; }
 };
+// word(i) selects with comparisons rather than indexing the vector: an index
+// known only at run time (the split-K kernel's batch phase) would otherwise
+// send the vector to scratch memory.
 template <>
 struct SEnt<64> {
     u32x2 v;
-    __device__ uint32_t word(int i) const { return v[i]; }
+    __device__ uint32_t word(int i) const { return i ? v[1] : v[0]; }
 };
 template <>
 struct SEnt<32> {
     u32x4 v;
-    __device__ uint32_t word(int i) const { return v[i]; }
+    __device__ uint32_t word(int i) const {
+        const uint32_t lo = (i & 1) ? v[1] : v[0];
+        const uint32_t hi = (i & 1) ? v[3] : v[2];
+        return (i & 2) ? hi : lo;
+    }
 };
 
 template <int G>
