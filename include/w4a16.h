@@ -63,13 +63,14 @@ typedef enum {
  * benchmarks and tests.  Give the same flags to w4a16_workspace_bytes and to
  * the GEMM call.  A hint that does not apply to the shape is ignored (the
  * default choice is made).  W4A16_PLAN_PARAM(n), n in 1..255, sets the
- * variant's parameter: the decode kernel's workgroup count, split-K
+ * variant's parameter: the decode or wide kernel's workgroup count, split-K
  * workgroups in units of 8, or the tiled kernel's split count.
  */
 #define W4A16_PLAN_DECODE 0x10u   /* streaming kernel for M <= 8, X held in LDS */
 #define W4A16_PLAN_SPLITK 0x20u   /* split-K streaming kernel (M <= 32) */
 #define W4A16_PLAN_TILED  0x30u   /* LDS-tiled MFMA kernel */
-#define W4A16_PLAN_MASK   0x30u
+#define W4A16_PLAN_WIDE   0x40u   /* block-streaming kernel for 32 < M <= 128 */
+#define W4A16_PLAN_MASK   0x70u
 #define W4A16_PLAN_PARAM_SHIFT 8
 #define W4A16_PLAN_PARAM(n) (((uint32_t)(n) & 0xFFu) << W4A16_PLAN_PARAM_SHIFT)
 #define W4A16_PLAN_BITS   (W4A16_PLAN_MASK | (0xFFu << W4A16_PLAN_PARAM_SHIFT))
@@ -155,7 +156,11 @@ size_t w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int group_size, ui
  * the workspace); other M <= 32 use a split-K streaming
  * kernel (every wave streams an equal contiguous share of the weight chunks;
  * partial sums of a split column block are reduced in a fixed order);
- * larger M uses an LDS-tiled MFMA kernel.  All reduce in a fixed order, so
+ * 32 < M <= 128 uses a block-streaming kernel (each workgroup streams whole
+ * 128-column blocks, its waves 4 tiles x 2 halves of K, the activations
+ * staged through LDS; K is split across workgroups through the workspace
+ * when there are fewer blocks than CUs); larger M uses an LDS-tiled MFMA
+ * kernel.  All reduce in a fixed order, so
  * results are bitwise reproducible run to run, and all use
  * v_mfma_f32_32x32x16.
  * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP.

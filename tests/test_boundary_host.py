@@ -97,6 +97,12 @@ def test_plan_hints(lib):
     # area plus 2 x 128 partial tiles of 8 rows x 32 columns (fp32)
     assert w4.w4a16_workspace_bytes(4, 28672, 8192, 128, f) == 65536 + 2 * 128 * 1024
     assert w4.w4a16_workspace_bytes(4, 28672, 8192, 128, f | w4.plan_flags(("decode", 224))) == 0
+    # wide kernel: 224 blocks of 128 columns fill the workgroups, no workspace;
+    # 64 blocks are split into 4 parts (4 tiles x 2 row tiles x 16 x 64 floats each)
+    assert w4.w4a16_workspace_bytes(64, 28672, 8192, 128, f | w4.plan_flags("wide")) == 0
+    assert w4.w4a16_workspace_bytes(64, 8192, 8192, 128, f | w4.plan_flags("wide")) == \
+        65536 + 64 * 4 * (4 * 2 * 16 * 64 * 4)
+    assert w4.plan_flags("wide") == 0x40
     assert w4.w4a16_workspace_bytes(4, 4096, 8192, 128, f | w4.plan_flags(("tiled", 4))) > 0
     # decode holds X in LDS: M = 8 rows of K = 16384 do not fit, the hint is ignored
     assert w4.w4a16_workspace_bytes(8, 4096, 1 << 14, 128, f | w4.plan_flags("decode")) == \
@@ -119,7 +125,7 @@ def gemm(lib, X=FAKE, packed=FAKE, pbytes=1 << 40, Y=FAKE, M=8, N=4096, K=4096, 
     (dict(N=0), w4.W4A16_ERR_INVALID_ARG),
     (dict(N=4000), w4.W4A16_ERR_UNSUPPORTED),            # N % 128
     (dict(K=4224), w4.W4A16_ERR_UNSUPPORTED),            # K % 256
-    (dict(flags=0x40), w4.W4A16_ERR_INVALID_ARG),        # neither a blob flag nor a plan hint
+    (dict(flags=0x80), w4.W4A16_ERR_INVALID_ARG),        # neither a blob flag nor a plan hint
 
     (dict(G=256), w4.W4A16_ERR_UNSUPPORTED),
     (dict(G=16), w4.W4A16_ERR_UNSUPPORTED),

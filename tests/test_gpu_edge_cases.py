@@ -36,6 +36,8 @@ CASES = [
     ("splitk", 1, 2048, 512, 128),
     (("splitk", 3), 7, 1024, 256, 64),
     (("splitk", 2), 30, 1024, 384, 32),
+    ("wide", 40, 2048, 512, 128),
+    (("wide", 16), 100, 1024, 384, 64),
     ("tiled", 48, 2048, 512, 128),
     (("tiled", 2), 130, 1024, 1024, 64),
 ]

@@ -2,7 +2,8 @@
 y = aux_op(act(X.deq * col_scale + bias), aux), against the CPU oracle's
 epilogue on the oracle's product.  Every kernel path that stores Y is covered:
 the decode kernel (one workgroup per tile, and one workgroup running many
-items in turn), split-K whole blocks, split-K blocks shared inside a workgroup
+items in turn), the wide kernel (whole blocks, and blocks split into parts
+that meet in the workspace), split-K whole blocks, split-K blocks shared inside a workgroup
 and between workgroups, the tiled kernel with and without a split of K.
 
 Bar: max |Y - Y_ref| / Bo <= 2e-3 (fp16) or 1e-2 (bf16), where Bo carries the
@@ -32,6 +33,8 @@ PATHS = [
     ("decode-m1", 1, 2048, 512, 128, "decode"),
     ("decode-m8-one-wg", 8, 1024, 768, 64, ("decode", 1)),
     ("decode-m7-split", 7, 1024, 384, 32, ("decode", 5)),
+    ("wide-m64", 64, 2048, 512, 128, "wide"),
+    ("wide-m100-parts", 100, 1024, 256, 64, ("wide", 16)),
     ("splitk-whole-blocks", 3, 2048, 512, 128, "splitk"),
     ("splitk-shared-blocks", 5, 1024, 256, 64, ("splitk", 3)),
     ("splitk-m32", 32, 1024, 384, 32, ("splitk", 2)),

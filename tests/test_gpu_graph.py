@@ -18,10 +18,12 @@ def _gpu():
         pytest.skip("no GPU")
 
 
-# (plan, M, K, N): the decode kernel (several items per workgroup), split-K
+# (plan, M, K, N): the decode kernel (several items per workgroup), the wide
+# kernel (whole blocks, and K split into parts across workgroups), split-K
 # with column blocks shared between workgroups, split-K with whole blocks, the
 # tiled kernel with split K
 CASES = [("decode", 1, 8192, 28672), (("decode", 3), 4, 2048, 1024),
+         ("wide", 64, 4096, 1024), (("wide", 255), 100, 2048, 512),
          ("splitk", 1, 4096, 4096), ("splitk", 8, 8192, 8192), ("splitk", 3, 1024, 28672),
          ("tiled", 70, 4096, 1024)]
 

@@ -142,6 +142,7 @@ def one_hot_rows(M, K, dtype):
 
 @pytest.mark.parametrize("variant,M", [("decode", 1), ("decode", 8), ("decode", 5),
                                        ("splitk", 1), ("splitk", 7), ("splitk", 32),
+                                       ("wide", 33), ("wide", 64), ("wide", 100), ("wide", 128),
                                        ("tiled", 20), ("tiled", 64), ("tiled", 130)])
 @pytest.mark.parametrize("K,N,G,dtype,sym", [(512, 384, 128, "fp16", False),
                                              (256, 256, 32, "bf16", False),
@@ -158,13 +159,13 @@ def test_gemm_one_hot_rows_are_dequantized_weights(variant, M, K, N, G, dtype, s
     assert same_bits(Y, deq[ks])
 
 
-@pytest.mark.parametrize("variant,M", [("decode", 3), ("splitk", 3), ("tiled", 70)])
+@pytest.mark.parametrize("variant,M", [("decode", 3), ("splitk", 3), ("wide", 70), ("tiled", 70)])
 def test_gemm_exact_bf16_form_for_huge_scales(variant, M):
     """bf16 scales so large that -z*s overflows fp32 (z = 15, s near 2^125) while
     every (q - z) * s stays finite (q in {14, 15}): the repack flags the blob and
     both kernels must still return the dequantized weights bit for bit."""
     w4 = lib()
-    K, N, G = 256, 256, 64
+    K, N, G = 512, 256, 64
     rng = np.random.default_rng(M)
     q = rng.integers(14, 16, size=(K, N)).astype(np.uint8)
     scales = rng.integers(0x7E00, 0x7E80, size=(K // G, N)).astype(np.uint16)   # 2^125..2^126
@@ -205,6 +206,8 @@ def test_gemm_matches_oracle(M, K, N, G, dtype, sym):
                                              ("decode", 6, 2), ("decode", 2, 255), ("decode", 3, 16),
                                              ("splitk", 4, 1), ("splitk", 4, 3), ("splitk", 30, 16),
                                              ("splitk", 1, 7), ("splitk", 9, 100), ("splitk", 2, 255),
+                                             ("wide", 48, 1), ("wide", 64, 3), ("wide", 70, 16),
+                                             ("wide", 128, 255), ("wide", 40, 255),
                                              ("tiled", 8, 1), ("tiled", 32, 2), ("tiled", 96, 5),
                                              ("tiled", 200, 16)])
 def test_gemm_forced_variant_and_param(variant, M, param):
@@ -212,7 +215,9 @@ def test_gemm_forced_variant_and_param(variant, M, param):
     output tiles (1 = one workgroup runs every item in turn, so the item slots
     are reused many times; 3, 7, 16: left-over tiles split along K in two
     halves, the split items first; 255: every tile in two halves); split-K:
-    8*param workgroups (2040 = more than there are batches); tiled: `param`
+    8*param workgroups (2040 = more than there are batches); wide: `param`
+    workgroups (1 and 3: every block in turn; 16 and 255: each of the five
+    blocks' K split into parts that meet in the workspace); tiled: `param`
     K-splits."""
     K, N, G = 4096, 640, 64
     p = synth.make_problem(M, K, N, G=G, dtype="bf16", sym=False, seed=M)
@@ -237,6 +242,7 @@ def test_workspace_counters_return_to_zero():
                                         (70, 8192, 384, "tiled"), (2, 8192, 4096, "splitk"),
                                         (1, 4096, 256, "splitk"), (5, 8192, 8192, "splitk"),
                                         (1, 4096, 1024, "decode"), (8, 8192, 4096, "decode"),
+                                        (64, 4096, 512, "wide"), (100, 2048, 1024, "wide"),
                                         (4, 2048, 512, "splitk")]):
         p = synth.make_problem(M, K, N, G=128, seed=i)
         say(f"workspace reuse call {i}: M={M} K={K} N={N} {var}")

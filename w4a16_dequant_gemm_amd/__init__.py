@@ -30,7 +30,7 @@ W4A16_BF16 = 0x1
 W4A16_ASYM = 0x0
 W4A16_SYM = 0x2
 # plan hints (flags of w4a16_workspace_bytes and the GEMM calls only)
-W4A16_PLAN = {"decode": 0x10, "splitk": 0x20, "tiled": 0x30}
+W4A16_PLAN = {"decode": 0x10, "splitk": 0x20, "tiled": 0x30, "wide": 0x40}
 W4A16_PLAN_PARAM_SHIFT = 8
 
 

@@ -22,7 +22,7 @@ COMMON = [
     "-Wall",
 ]
 
-# (source, extra defines): w4a16_gemm.hip and w4a16_decode.hip are compiled
+# (source, extra defines): the kernel sources are compiled
 # once per (activation dtype, epilogue) pair so that their kernel
 # instantiations compile in parallel.
 UNITS = [
@@ -37,6 +37,10 @@ UNITS = [
     ("w4a16_decode.hip", ["-DW4A16_TU_BF16=1", "-DW4A16_TU_EP=0"]),
     ("w4a16_decode.hip", ["-DW4A16_TU_BF16=0", "-DW4A16_TU_EP=1"]),
     ("w4a16_decode.hip", ["-DW4A16_TU_BF16=1", "-DW4A16_TU_EP=1"]),
+    ("w4a16_wide.hip", ["-DW4A16_TU_BF16=0", "-DW4A16_TU_EP=0"]),
+    ("w4a16_wide.hip", ["-DW4A16_TU_BF16=1", "-DW4A16_TU_EP=0"]),
+    ("w4a16_wide.hip", ["-DW4A16_TU_BF16=0", "-DW4A16_TU_EP=1"]),
+    ("w4a16_wide.hip", ["-DW4A16_TU_BF16=1", "-DW4A16_TU_EP=1"]),
 ]
 
 

@@ -82,6 +82,14 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int G, uint32_t flags) {
     auto decode_fits = [&](int tpi) {
         return M <= kDecodeMaxRows && decode_lds_bytes(M, K, tpi, kDecodeMaxRows) <= kDecodeLdsMax;
     };
+    // The wide kernel serves 32 < M <= 128 (its steps need K to hold at least
+    // one step per half).  Measured on MI355X (K = 8192, fp16): faster than
+    // the tiled kernel for M <= 96 (N = 28672 M = 96: 74-77 vs 83 us), and
+    // for every M up to 128 when the 128-column blocks cover at most half
+    // of the CUs (N = 8192: 31-49 vs 41-77 us); at N = 28672 M = 128 the
+    // tiled kernel is faster (85 vs 90-95 us).
+    const bool wide_fits = M >= kWideMinRows && M <= kWideMaxRows && K >= 2 * wide_step_k(M);
+    const bool wide_default = wide_fits && (M <= 96 || NB * 2 <= cus);
     Variant v;
     if (hint == W4A16_PLAN_DECODE && decode_fits(1))
         v = VARIANT_DECODE;
@@ -89,10 +97,14 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int G, uint32_t flags) {
         v = VARIANT_SPLITK;
     else if (hint == W4A16_PLAN_TILED)
         v = VARIANT_TILED;
+    else if (hint == W4A16_PLAN_WIDE && wide_fits)
+        v = VARIANT_WIDE;
     else if (decode_fits(1))
         v = VARIANT_DECODE;
     else if (M <= 32)
         v = VARIANT_SPLITK;
+    else if (wide_default)
+        v = VARIANT_WIDE;
     else
         v = VARIANT_TILED;
 
@@ -118,6 +130,26 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int G, uint32_t flags) {
         p.splits = (int)S;
         p.tiles = S > 1 ? (int)R : 0;
         p.tile_floats = (size_t)64 * 4;   // one part: 8 rows x 32 columns (64 lanes x 4)
+    } else if (v == VARIANT_WIDE) {
+        // Items of one 128-column block over all of K, one workgroup per CU
+        // (or the forced count), round-robin; with fewer blocks than
+        // workgroups each block's K is split into S parts (at most 8, and at
+        // most one per two steps of K), one workgroup per (block, part).
+        p.variant = VARIANT_WIDE;
+        p.items = (int)NB;
+        p.waves = kWideWaves;
+        int64_t W = cus;
+        if (hint == W4A16_PLAN_WIDE && param > 0) W = param;   // forced workgroup count
+        const int64_t T = K / wide_step_k(M);
+        int64_t S = NB < W ? std::min<int64_t>({W / NB, T / 2, 8}) : 1;
+        if (S < 2 || NB > kMaxTilesSplit) S = 1;
+        p.grid_x = (int)(S > 1 ? NB * S : std::min<int64_t>(NB, W));
+        p.grid_y = 1;
+        p.grid_z = 1;
+        p.splits = (int)S;
+        p.tiles = S > 1 ? (int)NB : 0;
+        // one part of a block: 4 tiles x (32-row tiles) x 16 registers x 64 lanes
+        p.tile_floats = (size_t)4 * ((M + 31) / 32) * 16 * 64;
     } else if (v == VARIANT_SPLITK) {
         // Balanced contiguous ranges of batches for every wave of one
         // workgroup per CU (fewer workgroups when there are fewer batches).
@@ -213,6 +245,13 @@ hipError_t launch_gemm(const void* X, const void* packed, void* Y, int64_t M, co
                           : launch_decode_bf16(X, packed, Y, M, L, plan, workspace, ep, stream);
         return ep.any ? launch_decode_f16_ep(X, packed, Y, M, L, plan, workspace, ep, stream)
                       : launch_decode_f16(X, packed, Y, M, L, plan, workspace, ep, stream);
+    }
+    if (plan.variant == VARIANT_WIDE) {
+        if (bf16)
+            return ep.any ? launch_wide_bf16_ep(X, packed, Y, M, L, plan, workspace, ep, stream)
+                          : launch_wide_bf16(X, packed, Y, M, L, plan, workspace, ep, stream);
+        return ep.any ? launch_wide_f16_ep(X, packed, Y, M, L, plan, workspace, ep, stream)
+                      : launch_wide_f16(X, packed, Y, M, L, plan, workspace, ep, stream);
     }
     if (bf16)
         return ep.any ? launch_gemm_bf16_ep(X, packed, Y, M, L, plan, workspace, ep, stream)

@@ -13,7 +13,7 @@ namespace w4a16 {
 // The split-K and tiled kernels work on column blocks of four tiles.
 constexpr int kColBlock = 4 * kTileCols;
 
-enum Variant { VARIANT_SPLITK = 0, VARIANT_TILED = 1, VARIANT_DECODE = 2 };
+enum Variant { VARIANT_SPLITK = 0, VARIANT_TILED = 1, VARIANT_DECODE = 2, VARIANT_WIDE = 3 };
 
 // Split-K kernel geometry, shared by the plan and the kernel.
 constexpr int kSplitKWaves = 8;   // waves per workgroup (two per SIMD), one workgroup per CU
@@ -37,6 +37,17 @@ constexpr bool kDecodeBalance = true;
 constexpr bool kDecodeScaleAfter = true;
 // LDS budget of the decode kernel (X rows + partial-tile slots), per workgroup.
 constexpr size_t kDecodeLdsMax = 160 * 1024;
+
+// Wide kernel (32 < M <= 128): 8 waves = 4 tiles x 2 halves of K per
+// workgroup; steps of 256 k for M <= 64, 128 k above.
+constexpr int kWideWaves = 8;
+constexpr int kWideMinRows = 33;
+constexpr int kWideMaxRows = 128;
+constexpr int kWidePrefetch = 1;   // weight steps in flight per wave (2 or 3 measured no faster)
+inline int wide_step_k(int64_t M) { return M <= 64 ? 256 : 128; }
+// LDS bytes of a wide launch: two slots of [2 halves][M rows][2*SK + 16
+// bytes] and a flag.
+inline size_t wide_lds_bytes(int64_t M, int sk) { return (size_t)4 * M * (2 * sk + 16) + 16; }
 
 // LDS bytes of a decode launch: M rows of X (2K bytes + 16 padding each), the
 // [2 items][waves][tiles per item][row groups][64 lanes] fp32x4 partial-tile
@@ -128,6 +139,10 @@ W4A16_DECLARE_DECODE_PART(launch_decode_f16)
 W4A16_DECLARE_DECODE_PART(launch_decode_f16_ep)
 W4A16_DECLARE_DECODE_PART(launch_decode_bf16)
 W4A16_DECLARE_DECODE_PART(launch_decode_bf16_ep)
+W4A16_DECLARE_DECODE_PART(launch_wide_f16)
+W4A16_DECLARE_DECODE_PART(launch_wide_f16_ep)
+W4A16_DECLARE_DECODE_PART(launch_wide_bf16)
+W4A16_DECLARE_DECODE_PART(launch_wide_bf16_ep)
 #undef W4A16_DECLARE_DECODE_PART
 // Read-bandwidth probe geometry: one workgroup of 8 waves per CU.
 constexpr int kProbeBlocks = 256;
