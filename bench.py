@@ -126,7 +126,8 @@ def cpu_baseline(name, cfg, budget_s=12.0):
     }
 
 
-KERNEL_SOURCES = ("w4a16_gemm.hip", "w4a16_decode.hip", "w4a16_device.h", "w4a16_epilogue.h",
+KERNEL_SOURCES = ("w4a16_gemm.hip", "w4a16_decode.hip", "w4a16_wide.hip", "w4a16_device.h",
+                  "w4a16_epilogue.h",
                   "w4a16_layout.h", "w4a16_internal.h", "w4a16_api.cpp")
 # Reported beside the headline workload (same protocol, no CPU baseline or
 # comparators): the prefill and the batched shapes of the same layer.
