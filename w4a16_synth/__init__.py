@@ -33,7 +33,8 @@ from typing import Optional
 import numpy as np
 
 __all__ = ["Problem", "make_problem", "make_weights", "make_activations", "with_activations",
-           "pack_nibbles", "to_dtype_bits", "WORKLOADS", "workload"]
+           "pack_nibbles", "to_dtype_bits", "WORKLOADS", "workload", "ProblemW8",
+           "make_w4a8_weights", "make_w4a8_activations", "make_w4a8_problem", "W4A8_WORKLOADS"]
 
 
 def to_dtype_bits(x64: np.ndarray, dtype: str) -> np.ndarray:
@@ -149,3 +150,63 @@ WORKLOADS = {
 
 def workload(name: str, seed: int = 0, keep_q: bool = False) -> Problem:
     return make_problem(seed=seed, keep_q=keep_q, **WORKLOADS[name])
+
+
+# ---------------------------------------------------------------------------
+# W4A8 route inputs.  Random draws only, inside the format's valid ranges:
+#   xq   int8 [M][K], uniform integers in [-127, 127]   (stream 0)
+#   sx   float32 [M], U(0.001, 0.02)                     (stream 4)
+#   q    uint8 [K][N], uniform integers 0..15, packed like qweight above (stream 1)
+#   s8   uint8 [K/G][N], uniform integers in [s_lo, 16]  (stream 2)
+#   a    uint8 [K/G][N], uniform integers in [0, 255 - 15*s8] (stream 3), the
+#        offsets for which no code can pass 255
+#   sw   float32 [N], U(0.0005, 0.005)                   (stream 2, after s8)
+# ---------------------------------------------------------------------------
+
+@dataclass
+class ProblemW8:
+    M: int
+    K: int
+    N: int
+    G: int
+    xq: np.ndarray        # int8 [M][K]
+    sx: np.ndarray        # float32 [M]
+    qweight: np.ndarray   # uint32 [K/8][N]
+    s8: np.ndarray        # uint8 [K/G][N]
+    a: np.ndarray         # uint8 [K/G][N]
+    sw: np.ndarray        # float32 [N]
+
+
+def make_w4a8_weights(K: int, N: int, G: int = 128, seed: int = 0, s_lo: int = 1):
+    """(qweight, s8, a, sw) for the W4A8 route."""
+    if K % 8 or K % G:
+        raise ValueError("K must be a multiple of 8 and of G")
+    st = _streams(seed)
+    q = st[1].integers(0, 16, size=(K, N), dtype=np.uint8)
+    s8 = st[2].integers(s_lo, 17, size=(K // G, N), dtype=np.int64)
+    a = np.floor(st[3].random((K // G, N)) * (256 - 15 * s8)).astype(np.int64)
+    sw = st[2].uniform(0.0005, 0.005, size=N).astype(np.float32)
+    return pack_nibbles(q), s8.astype(np.uint8), a.astype(np.uint8), sw
+
+
+def make_w4a8_activations(M: int, K: int, seed: int = 0):
+    """(xq int8 [M][K], sx float32 [M])."""
+    st = _streams(seed)
+    xq = st[0].integers(-127, 128, size=(M, K), dtype=np.int64).astype(np.int8)
+    sx = st[4].uniform(0.001, 0.02, size=M).astype(np.float32)
+    return xq, sx
+
+
+def make_w4a8_problem(M: int, K: int, N: int, G: int = 128, seed: int = 0) -> ProblemW8:
+    qweight, s8, a, sw = make_w4a8_weights(K, N, G, seed)
+    xq, sx = make_w4a8_activations(M, K, seed)
+    return ProblemW8(M, K, N, G, xq, sx, qweight, s8, a, sw)
+
+
+# The W4A8 workloads: the same 70B-class layer; batch 128 is where the pages
+# switch to the compute-bound mode, 4096 rows a prefill.
+W4A8_WORKLOADS = {
+    "w4a8_decode_m1_k8192_n28672_g128": dict(M=1, K=8192, N=28672, G=128),
+    "w4a8_batch_m128_k8192_n28672_g128": dict(M=128, K=8192, N=28672, G=128),
+    "w4a8_prefill_m4096_k8192_n28672_g128": dict(M=4096, K=8192, N=28672, G=128),
+}
