@@ -10,7 +10,8 @@ import tempfile
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libw4a16.so")
-HEADERS = ["w4a16_layout.h", "w4a16_device.h", "w4a16_internal.h", "w4a16_epilogue.h"]
+HEADERS = ["w4a16_layout.h", "w4a16_device.h", "w4a16_internal.h", "w4a16_epilogue.h",
+           "w4a8_internal.h", "w4a8_device.h"]
 
 COMMON = [
     "--offload-arch=gfx950",
@@ -41,6 +42,11 @@ UNITS = [
     ("w4a16_wide.hip", ["-DW4A16_TU_BF16=1", "-DW4A16_TU_EP=0"]),
     ("w4a16_wide.hip", ["-DW4A16_TU_BF16=0", "-DW4A16_TU_EP=1"]),
     ("w4a16_wide.hip", ["-DW4A16_TU_BF16=1", "-DW4A16_TU_EP=1"]),
+    ("w4a8_api.cpp", []),
+    ("w4a8_prep.hip", []),
+    ("w4a8_gemm.hip", ["-DW4A8_TU_OUT=0"]),
+    ("w4a8_gemm.hip", ["-DW4A8_TU_OUT=1"]),
+    ("w4a8_gemm.hip", ["-DW4A8_TU_OUT=2"]),
 ]
 
 

@@ -1,0 +1,385 @@
+// w4a8_gemm.hip -- the W4A8 GEMM kernels for gfx950: 4-bit codes streamed
+// from HBM, turned into int8 in registers (one v_pk_mad_u16 and one
+// v_xor_b32 per four weights), v_mfma_i32_32x32x32_i8 with int32
+// accumulation, the per-row and per-column fp32 scales applied once per
+// output after the sum.
+//
+// Page "W4A8量化计算优化：提升LLM推理效率的关键技术": section 2.1 (the u4 -> i8
+// step), section 2.2 (one 128-bit load per lane feeds two matrix
+// instructions: here one global_load_dwordx4 per lane holds a tile's B
+// operands for two k-steps), section 4.2 (a memory-bound kernel for small
+// batches and a compute-bound one above).  Page "量化开销对比", section 1
+// (route A: int8 x int8 -> int32 -> scale) and section 2 (symmetric scales
+// leave the integer sum as the only term).
+//
+// Compiled once per output kind (W4A8_TU_OUT = 0 fp16, 1 bf16, 2 int32).
+#include <hip/hip_runtime.h>
+
+#include "w4a8_device.h"
+#include "w4a8_internal.h"
+
+#ifndef W4A8_TU_OUT
+#define W4A8_TU_OUT 0
+#endif
+
+namespace w4a8 {
+
+namespace {
+
+template <int OUT>
+__device__ __forceinline__ void store_out(void* Y, int64_t idx, int acc, float sxm, float swn) {
+    if constexpr (OUT == OUT_I32) {
+        ((int*)Y)[idx] = acc;
+    } else {
+        const float v = ((float)acc * sxm) * swn;
+        uint16_t b;
+        if constexpr (OUT == OUT_F16)
+            b = __builtin_bit_cast(uint16_t, (_Float16)v);
+        else
+            b = __builtin_bit_cast(uint16_t, (__bf16)v);
+        ((uint16_t*)Y)[idx] = b;
+    }
+}
+
+// Group constants of k-step s of chunk c: G32 -> group 2c + s, else
+// group c >> gshift (gshift = log2(G / 64)).
+template <bool G32>
+__device__ __forceinline__ int group_of(int c, int s, int gshift) {
+    return G32 ? 2 * c + s : (c >> gshift);
+}
+
+// ---------------------------------------------------------------------------
+// Streaming kernel (M <= 64).  Wave w of a workgroup works on tile
+// blockIdx.x * (8/KP) + w / KP over part w % KP of the chunks.  Per chunk a
+// lane loads its 16 bytes of weights (the next P chunks are in flight), the
+// group constants, and its 16 bytes of X per row tile and k-step; then two
+// k-steps of RT MFMAs.  The KP parts of a tile add up in LDS.
+// ---------------------------------------------------------------------------
+constexpr int kStreamDepth = 4;   // weight chunks in flight per wave
+
+template <int RT, int KP, bool G32, int OUT>
+__global__ __launch_bounds__(kW8Waves * 64) void w8_stream_kernel(
+    const int8_t* __restrict__ X, const float* __restrict__ sx, const uint8_t* __restrict__ blob,
+    void* __restrict__ Y, int M, int N, int K, int gshift, size_t m_off, size_t c_off) {
+    constexpr int CTW = kW8Waves / KP;
+    constexpr int P = kStreamDepth;
+    extern __shared__ int red[];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int part = wave % KP;
+    const int ctl = wave / KP;
+    const int KC = K / kChunkK;
+    const int NG = G32 ? K / 32 : (K / kChunkK) >> gshift;
+    const int t = blockIdx.x * CTW + ctl;
+    const int per = (KC + KP - 1) / KP;
+    const int c0 = min(part * per, KC);
+    const int c1 = min(c0 + per, KC);
+    const int n = c1 - c0;   // chunks of this wave (0 only if KC < KP, which the plan avoids)
+
+    const u32x4* wsrc = (const u32x4*)blob + (size_t)t * KC * 64 + lane;
+    const uint16_t* msrc = (const uint16_t*)(blob + m_off) + (size_t)t * NG * 32 + (lane & 31);
+    const int8_t* xsrc[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+        xsrc[r] = X + (size_t)min(32 * r + (lane & 31), M - 1) * K + 16 * (lane >> 5);
+
+    i32x16 acc[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[r][i] = 0;
+
+    // weight ring: slot i holds chunk c0 + (base + i)
+    u32x4 wb[P];
+#pragma unroll
+    for (int i = 0; i < P; ++i) wb[i] = __builtin_nontemporal_load(wsrc + (size_t)min(c0 + i, c1 - 1) * 64);
+
+    for (int base = 0; base < n; base += P) {
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            const int c = c0 + base + i;
+            if (base + i < n) {
+                i32x4 xa[RT][2];
+#pragma unroll
+                for (int r = 0; r < RT; ++r) {
+                    xa[r][0] = *(const i32x4*)(xsrc[r] + (size_t)c * kChunkK);
+                    xa[r][1] = *(const i32x4*)(xsrc[r] + (size_t)c * kChunkK + 32);
+                }
+                const uint32_t m0 = msrc[(size_t)group_of<G32>(c, 0, gshift) * 32];
+                const uint32_t m1 = G32 ? msrc[(size_t)group_of<G32>(c, 1, gshift) * 32] : m0;
+                const u32x4 w = wb[i];
+                wb[i] = __builtin_nontemporal_load(wsrc + (size_t)min(c + P, c1 - 1) * 64);
+                const i32x4 b0 = operand_b(w[0], w[1], group_w8(m0));
+                const i32x4 b1 = operand_b(w[2], w[3], group_w8(m1));
+#pragma unroll
+                for (int r = 0; r < RT; ++r)
+                    acc[r] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xa[r][0], b0, acc[r], 0, 0, 0);
+#pragma unroll
+                for (int r = 0; r < RT; ++r)
+                    acc[r] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xa[r][1], b1, acc[r], 0, 0, 0);
+            }
+        }
+    }
+
+    if constexpr (KP > 1) {
+        // parts 1..KP-1 leave their sums in LDS; part 0 adds them
+        if (part > 0) {
+#pragma unroll
+            for (int r = 0; r < RT; ++r)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    red[((((part - 1) * CTW + ctl) * RT + r) * 16 + i) * 64 + lane] = acc[r][i];
+        }
+        __syncthreads();
+        if (part > 0) return;
+#pragma unroll 1
+        for (int p = 1; p < KP; ++p)
+#pragma unroll
+            for (int r = 0; r < RT; ++r)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    acc[r][i] += red[((((p - 1) * CTW + ctl) * RT + r) * 16 + i) * 64 + lane];
+    }
+
+    const int col = t * kTileCols + (lane & 31);
+    const float swn = OUT == OUT_I32 ? 0.0f : ((const float*)(blob + c_off))[col];
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int row = 32 * r + acc_row_w8(i, lane);
+            if (row < M) store_out<OUT>(Y, (int64_t)row * N + col, acc[r][i],
+                                        OUT == OUT_I32 ? 0.0f : sx[row], swn);
+        }
+}
+
+// ---------------------------------------------------------------------------
+// Tiled kernel (M > 64).  A workgroup owns BM = WM*RT*32 rows and BN =
+// WN*CT*32 columns over all of K.  Per chunk (64 of K) the workgroup copies
+// its BM x 64 bytes of X into one slot of a two-slot LDS ring (rows padded to
+// 80 bytes: the 16-byte operand reads of 16 consecutive rows then cover all
+// 64 banks once), while each wave turns its CT tiles' codes into int8 B
+// operands in registers (the next chunk's codes already in flight) and runs
+// RT x CT x 2 MFMAs with A operands read from LDS.  One barrier per chunk.
+// Tiles are ordered so that the workgroups resident on one XCD at a time
+// share rows of X and columns of W in that XCD's L2.
+// ---------------------------------------------------------------------------
+template <int RT, int CT, int WM, int WN, bool G32, int OUT>
+__global__ __launch_bounds__(kW8Waves * 64) void w8_tiled_kernel(
+    const int8_t* __restrict__ X, const float* __restrict__ sx, const uint8_t* __restrict__ blob,
+    void* __restrict__ Y, int M, int N, int K, int gshift, size_t m_off, size_t c_off, int nbm,
+    int nbn) {
+    static_assert(WM * WN == kW8Waves, "eight waves");
+    constexpr int BM = WM * RT * 32;
+    constexpr int BN = WN * CT * 32;
+    constexpr int RB = kTiledRowBytes;
+    constexpr int SLOT = BM * RB;
+    constexpr int PIECES = BM * 4 / (kW8Waves * 64);   // 16-byte X pieces per thread and chunk
+    static_assert(PIECES >= 1 && BM * 4 == PIECES * kW8Waves * 64, "X staging");
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave / WN;
+    const int wn = wave % WN;
+    const int KC = K / kChunkK;
+    const int NT = N / kTileCols;
+    const int NG = G32 ? K / 32 : KC >> gshift;
+
+    // task -> (row block, column block): first spread over the 8 XCDs in
+    // contiguous runs (dispatch goes round-robin over XCDs), then groups of 4
+    // row blocks walked column block by column block.
+    const int T = nbm * nbn;
+    int task = blockIdx.x;
+    if (T % 8 == 0) task = (blockIdx.x % 8) * (T / 8) + blockIdx.x / 8;
+    constexpr int GM = 4;
+    const int group = task / (GM * nbn);
+    const int first_m = group * GM;
+    const int gsz = min(nbm - first_m, GM);
+    const int in_group = task % (GM * nbn);
+    const int mb = first_m + in_group % gsz;
+    const int nb = in_group / gsz;
+    const int m0 = mb * BM;
+
+    int tile[CT];
+    bool tile_ok[CT];
+    const u32x4* wsrc[CT];
+    const uint16_t* msrc[CT];
+#pragma unroll
+    for (int j = 0; j < CT; ++j) {
+        const int tt = nb * (BN / 32) + wn * CT + j;
+        tile_ok[j] = tt < NT;
+        tile[j] = min(tt, NT - 1);
+        wsrc[j] = (const u32x4*)blob + (size_t)tile[j] * KC * 64 + lane;
+        msrc[j] = (const uint16_t*)(blob + m_off) + (size_t)tile[j] * NG * 32 + (lane & 31);
+    }
+
+    // X staging: piece p = tid + 512*i is row p/4, 16-byte quarter p%4.
+    const int8_t* xg[PIECES];
+    int xl[PIECES];
+#pragma unroll
+    for (int i = 0; i < PIECES; ++i) {
+        const int p = tid + kW8Waves * 64 * i;
+        const int row = p >> 2;
+        xg[i] = X + (size_t)min(m0 + row, M - 1) * K + 16 * (p & 3);
+        xl[i] = row * RB + 16 * (p & 3);
+    }
+    // A operand of row tile r, k-step s: row wm*RT*32 + 32r + lane%32, bytes 32s + 16*(lane/32)
+    const int arow = (wm * RT * 32 + (lane & 31)) * RB + 16 * (lane >> 5);
+
+    i32x16 acc[RT][CT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int j = 0; j < CT; ++j)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[r][j][i] = 0;
+
+    // prologue: X of chunk 0 into slot 0, codes of chunks 0 and 1 in flight
+    {
+        i32x4 xr[PIECES];
+#pragma unroll
+        for (int i = 0; i < PIECES; ++i) xr[i] = *(const i32x4*)xg[i];
+#pragma unroll
+        for (int i = 0; i < PIECES; ++i) *(i32x4*)(lds + xl[i]) = xr[i];
+    }
+    u32x4 wb[2][CT];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int j = 0; j < CT; ++j)
+            wb[q][j] = __builtin_nontemporal_load(wsrc[j] + (size_t)min(q, KC - 1) * 64);
+    __syncthreads();
+
+    for (int cb = 0; cb < KC; cb += 2) {   // KC is a multiple of 4
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int c = cb + q;
+            const uint8_t* slot = lds + q * SLOT;   // chunk c lives in slot c % 2 == q
+            // X of chunk c+1 (clamped; the last one is a harmless repeat)
+            i32x4 xr[PIECES];
+            const int cn = min(c + 1, KC - 1);
+#pragma unroll
+            for (int i = 0; i < PIECES; ++i) xr[i] = *(const i32x4*)(xg[i] + (size_t)cn * kChunkK);
+            // group constants of chunk c
+            uint32_t mt[CT][2];
+#pragma unroll
+            for (int j = 0; j < CT; ++j) {
+                mt[j][0] = msrc[j][(size_t)group_of<G32>(c, 0, gshift) * 32];
+                mt[j][1] = G32 ? msrc[j][(size_t)group_of<G32>(c, 1, gshift) * 32] : mt[j][0];
+            }
+            // B operands of chunk c, then the codes of chunk c+2 into the freed registers
+            i32x4 bq[CT][2];
+#pragma unroll
+            for (int j = 0; j < CT; ++j) {
+                const u32x4 w = wb[q][j];
+                bq[j][0] = operand_b(w[0], w[1], group_w8(mt[j][0]));
+                bq[j][1] = operand_b(w[2], w[3], group_w8(mt[j][1]));
+            }
+#pragma unroll
+            for (int j = 0; j < CT; ++j)
+                wb[q][j] = __builtin_nontemporal_load(wsrc[j] + (size_t)min(c + 2, KC - 1) * 64);
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                i32x4 a[RT];
+#pragma unroll
+                for (int r = 0; r < RT; ++r)
+                    a[r] = *(const i32x4*)(slot + arow + r * 32 * RB + 32 * s);
+#pragma unroll
+                for (int r = 0; r < RT; ++r)
+#pragma unroll
+                    for (int j = 0; j < CT; ++j)
+                        acc[r][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[r], bq[j][s],
+                                                                          acc[r][j], 0, 0, 0);
+            }
+            // slot (c+1) % 2 was last read in chunk c-1, before the previous barrier
+            uint8_t* next = lds + (1 - q) * SLOT;
+#pragma unroll
+            for (int i = 0; i < PIECES; ++i) *(i32x4*)(next + xl[i]) = xr[i];
+            __syncthreads();
+        }
+    }
+
+    const float* colscale = (const float*)(blob + c_off);
+#pragma unroll
+    for (int j = 0; j < CT; ++j) {
+        if (!tile_ok[j]) continue;
+        const int col = tile[j] * kTileCols + (lane & 31);
+        const float swn = OUT == OUT_I32 ? 0.0f : colscale[col];
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int row = m0 + wm * RT * 32 + 32 * r + acc_row_w8(i, lane);
+                if (row < M) store_out<OUT>(Y, (int64_t)row * N + col, acc[r][j][i],
+                                            OUT == OUT_I32 ? 0.0f : sx[row], swn);
+            }
+    }
+}
+
+template <int RT, int KP, bool G32>
+hipError_t launch_stream_t(const int8_t* xq, const float* sx, const void* packed, void* Y,
+                           int64_t M, const LayoutW8& L, const PlanW8& plan, int gshift,
+                           hipStream_t stream) {
+    w8_stream_kernel<RT, KP, G32, W4A8_TU_OUT><<<plan.grid, kW8Waves * 64, plan.lds, stream>>>(
+        xq, sx, (const uint8_t*)packed, Y, (int)M, (int)L.N, (int)L.K, gshift, L.m_off, L.c_off);
+    return hipGetLastError();
+}
+
+template <int RT, bool G32>
+hipError_t launch_stream_kp(const int8_t* xq, const float* sx, const void* packed, void* Y,
+                            int64_t M, const LayoutW8& L, const PlanW8& plan, int gshift,
+                            hipStream_t stream) {
+    switch (plan.kp) {
+        case 2: return launch_stream_t<RT, 2, G32>(xq, sx, packed, Y, M, L, plan, gshift, stream);
+        case 4: return launch_stream_t<RT, 4, G32>(xq, sx, packed, Y, M, L, plan, gshift, stream);
+        default: return launch_stream_t<RT, 8, G32>(xq, sx, packed, Y, M, L, plan, gshift, stream);
+    }
+}
+
+template <bool G32>
+hipError_t launch_g(const int8_t* xq, const float* sx, const void* packed, void* Y, int64_t M,
+                    const LayoutW8& L, const PlanW8& plan, int gshift, hipStream_t stream) {
+    const uint8_t* b = (const uint8_t*)packed;
+    if (plan.variant == W8_STREAM) {
+        if (plan.rt == 1)
+            return launch_stream_kp<1, G32>(xq, sx, packed, Y, M, L, plan, gshift, stream);
+        return launch_stream_kp<2, G32>(xq, sx, packed, Y, M, L, plan, gshift, stream);
+    }
+    if (plan.cfg == 0)
+        w8_tiled_kernel<4, 2, 2, 4, G32, W4A8_TU_OUT><<<plan.grid, kW8Waves * 64, plan.lds,
+                                                        stream>>>(
+            xq, sx, b, Y, (int)M, (int)L.N, (int)L.K, gshift, L.m_off, L.c_off, plan.nbm,
+            plan.nbn);
+    else
+        w8_tiled_kernel<2, 1, 2, 4, G32, W4A8_TU_OUT><<<plan.grid, kW8Waves * 64, plan.lds,
+                                                        stream>>>(
+            xq, sx, b, Y, (int)M, (int)L.N, (int)L.K, gshift, L.m_off, L.c_off, plan.nbm,
+            plan.nbn);
+    return hipGetLastError();
+}
+
+hipError_t launch_part(const int8_t* xq, const float* sx, const void* packed, void* Y, int64_t M,
+                       const LayoutW8& L, const PlanW8& plan, hipStream_t stream) {
+    if (L.G == 32) return launch_g<true>(xq, sx, packed, Y, M, L, plan, 0, stream);
+    const int gshift = L.G == 64 ? 0 : 1;
+    return launch_g<false>(xq, sx, packed, Y, M, L, plan, gshift, stream);
+}
+
+}  // namespace
+
+#if W4A8_TU_OUT == 0
+#define W4A8_PART_NAME launch_w8_gemm_f16
+#elif W4A8_TU_OUT == 1
+#define W4A8_PART_NAME launch_w8_gemm_bf16
+#else
+#define W4A8_PART_NAME launch_w8_gemm_i32
+#endif
+
+hipError_t W4A8_PART_NAME(const int8_t* xq, const float* sx, const void* packed, void* Y,
+                          int64_t M, const LayoutW8& L, const PlanW8& plan, hipStream_t stream) {
+    return launch_part(xq, sx, packed, Y, M, L, plan, stream);
+}
+
+}  // namespace w4a8
