@@ -57,7 +57,8 @@ extern "C" {
 #define W4A8_OUT_MASK 0x3u
 /* Plan hints (w4a8_gemm flags only; for tests and benchmarks).  A hint that
  * does not apply to the shape is ignored.  W4A16_PLAN_PARAM(n) sets the
- * streaming kernel's parts of K per tile (2, 4 or 8). */
+ * streaming kernel's parts of K per tile (2, 4 or 8), or the tiled kernel's
+ * workgroup tile (1: 256 x 256, 2: 128 x 128, 3: 256 x 128). */
 #define W4A8_PLAN_STREAM 0x10u   /* streaming kernel, M <= 64 */
 #define W4A8_PLAN_TILED  0x20u   /* LDS-tiled kernel */
 #define W4A8_PLAN_MASK   0x30u
@@ -117,8 +118,9 @@ w4a16_status_t w4a8_quantize_rows(const void *X, int8_t *xq, float *sx, int64_t 
  *   sx      dev, float [M] (may be NULL with W4A8_OUT_I32).
  *   packed  dev, a blob of w4a8_repack for (K, N, G).
  *   Y       dev, [M][N] of the output kind in flags.
- * Kernel choice (by M): the streaming kernel for M <= 64, the LDS-tiled
- * kernel above (workgroup tile 128 x 128 up to M = 512, 256 x 256 beyond).
+ * Kernel choice (by M): the streaming kernel for M <= 32, the LDS-tiled
+ * kernel above (workgroup tile 128 x 128 up to M = 128, 256 x 128 up to 512,
+ * 256 x 256 beyond).
  * No workspace.  Calls on one stream may run back to back; Y must not
  * overlap the inputs.
  * Errors: INVALID_ARG, UNSUPPORTED, HIP.

@@ -165,7 +165,9 @@ GEMM_CASES = [
     (64, 768, 128, 32, ("stream", 8)), (3, 512, 384, 128, "tiled"),
     (65, 512, 384, 128, None), (100, 1024, 256, 32, None), (130, 768, 640, 64, None),
     (300, 512, 128, 128, None), (513, 1024, 384, 128, None), (600, 256, 256, 32, None),
-    (1000, 512, 640, 64, None),
+    (1000, 512, 640, 64, None), (200, 512, 384, 32, ("tiled", 3)),
+    (40, 1024, 640, 64, ("tiled", 1)), (130, 512, 384, 128, ("tiled", 2)),
+    (257, 768, 128, 64, ("tiled", 1)), (48, 512, 256, 64, ("stream", 2)),
 ]
 
 

@@ -54,30 +54,44 @@ PlanW8 make_plan_w8(int64_t M, int64_t N, int64_t K, uint32_t flags, int cus) {
     const int64_t NT = N / kTileCols;
     const int64_t KC = K / kChunkK;
     const bool stream_ok = M <= kStreamMaxRows;
-    const bool stream = hint == W4A8_PLAN_TILED ? false : stream_ok;
+    const bool stream = hint == W4A8_PLAN_TILED    ? false
+                        : hint == W4A8_PLAN_STREAM ? stream_ok
+                                                   : M <= kStreamDefaultRows;
     if (stream) {
         p.variant = W8_STREAM;
         p.rt = M <= 32 ? 1 : 2;
         if ((param == 2 || param == 4 || param == 8) && KC >= param) {
             p.kp = param;
         } else {
-            // the fewest parts that still give two workgroups per CU
+            // M <= 8: the fewest parts that still give two workgroups per CU;
+            // M > 8: 4 parts (measured fastest on the 8192 x 28672 layer)
             p.kp = KC >= 8 ? 8 : 4;
-            for (int kp = 2; kp <= 8; kp *= 2)
-                if (NT * kp / kW8Waves >= 2 * (int64_t)cus && KC >= kp) {
-                    p.kp = kp;
-                    break;
-                }
+            if (M > 8) {
+                p.kp = 4;
+            } else {
+                for (int kp = 2; kp <= 8; kp *= 2)
+                    if (NT * kp / kW8Waves >= 2 * (int64_t)cus && KC >= kp) {
+                        p.kp = kp;
+                        break;
+                    }
+            }
         }
         const int ctw = kW8Waves / p.kp;
         p.grid = (int)(NT / ctw);
         p.lds = (size_t)(p.kp - 1) * ctw * p.rt * 16 * 64 * 4;
     } else {
         p.variant = W8_TILED;
-        p.cfg = M <= 512 ? 1 : 0;
-        const int64_t bm = p.cfg == 0 ? 256 : 128;
+        // tile shapes: 0 = 256 x 256 (4 x 2 tiles per wave), 1 = 128 x 128 (2 x 1),
+        // 2 = 256 x 128 (4 x 1); W4A16_PLAN_PARAM(1 + shape) forces one
+        // (measured on the 8192 x 28672 layer: 128 x 128 is fastest up to M = 128,
+        // 256 x 128 up to 512, 256 x 256 beyond)
+        p.cfg = (hint == W4A8_PLAN_TILED && param >= 1 && param <= 3) ? param - 1
+                : M <= 128                                            ? 1
+                : M <= 512                                            ? 2
+                                                                      : 0;
+        const int64_t bm = p.cfg == 1 ? 128 : 256;
         const int64_t bn = p.cfg == 0 ? 256 : 128;
-        p.rt = p.cfg == 0 ? 4 : 2;
+        p.rt = p.cfg == 1 ? 2 : 4;
         p.nbm = (int)((M + bm - 1) / bm);
         p.nbn = (int)((N + bn - 1) / bn);
         p.grid = p.nbm * p.nbn;

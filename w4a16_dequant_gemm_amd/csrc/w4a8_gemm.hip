@@ -22,6 +22,7 @@
 #define W4A8_TU_OUT 0
 #endif
 
+
 namespace w4a8 {
 
 namespace {
@@ -51,11 +52,12 @@ __device__ __forceinline__ int group_of(int c, int s, int gshift) {
 // ---------------------------------------------------------------------------
 // Streaming kernel (M <= 64).  Wave w of a workgroup works on tile
 // blockIdx.x * (8/KP) + w / KP over part w % KP of the chunks.  Per chunk a
-// lane loads its 16 bytes of weights (the next P chunks are in flight), the
-// group constants, and its 16 bytes of X per row tile and k-step; then two
-// k-steps of RT MFMAs.  The KP parts of a tile add up in LDS.
+// lane needs its 16 bytes of weights, the group constants and its 16 bytes of
+// X per row tile and k-step (X is small and stays in L2); all three ride in a
+// ring of P chunks in flight.  Then two k-steps of RT MFMAs.  The KP parts of
+// a tile add up in LDS.
 // ---------------------------------------------------------------------------
-constexpr int kStreamDepth = 4;   // weight chunks in flight per wave
+constexpr int kStreamDepth = 4;   // chunks in flight per wave
 
 template <int RT, int KP, bool G32, int OUT>
 __global__ __launch_bounds__(kW8Waves * 64) void w8_stream_kernel(
@@ -89,26 +91,40 @@ __global__ __launch_bounds__(kW8Waves * 64) void w8_stream_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[r][i] = 0;
 
-    // weight ring: slot i holds chunk c0 + (base + i)
+    // Ring of P chunks in flight: slot i holds chunk c0 + base + i -- its
+    // codes, its group constants and its X operands.  Slot i is refilled with
+    // chunk c + P as soon as chunk c has been copied out of it.
     u32x4 wb[P];
+    i32x4 xb[P][RT][2];
+    uint32_t mb[P][2];
+    auto fill = [&](int i, int c) __attribute__((always_inline)) {
+        wb[i] = __builtin_nontemporal_load(wsrc + (size_t)c * 64);
 #pragma unroll
-    for (int i = 0; i < P; ++i) wb[i] = __builtin_nontemporal_load(wsrc + (size_t)min(c0 + i, c1 - 1) * 64);
+        for (int r = 0; r < RT; ++r) {
+            xb[i][r][0] = *(const i32x4*)(xsrc[r] + (size_t)c * kChunkK);
+            xb[i][r][1] = *(const i32x4*)(xsrc[r] + (size_t)c * kChunkK + 32);
+        }
+        mb[i][0] = msrc[(size_t)group_of<G32>(c, 0, gshift) * 32];
+        mb[i][1] = G32 ? msrc[(size_t)group_of<G32>(c, 1, gshift) * 32] : 0u;
+    };
+#pragma unroll
+    for (int i = 0; i < P; ++i) fill(i, min(c0 + i, c1 - 1));
 
     for (int base = 0; base < n; base += P) {
 #pragma unroll
         for (int i = 0; i < P; ++i) {
             const int c = c0 + base + i;
             if (base + i < n) {
+                const u32x4 w = wb[i];
                 i32x4 xa[RT][2];
 #pragma unroll
                 for (int r = 0; r < RT; ++r) {
-                    xa[r][0] = *(const i32x4*)(xsrc[r] + (size_t)c * kChunkK);
-                    xa[r][1] = *(const i32x4*)(xsrc[r] + (size_t)c * kChunkK + 32);
+                    xa[r][0] = xb[i][r][0];
+                    xa[r][1] = xb[i][r][1];
                 }
-                const uint32_t m0 = msrc[(size_t)group_of<G32>(c, 0, gshift) * 32];
-                const uint32_t m1 = G32 ? msrc[(size_t)group_of<G32>(c, 1, gshift) * 32] : m0;
-                const u32x4 w = wb[i];
-                wb[i] = __builtin_nontemporal_load(wsrc + (size_t)min(c + P, c1 - 1) * 64);
+                const uint32_t m0 = mb[i][0];
+                const uint32_t m1 = G32 ? mb[i][1] : m0;
+                fill(i, min(c + P, c1 - 1));
                 const i32x4 b0 = operand_b(w[0], w[1], group_w8(m0));
                 const i32x4 b1 = operand_b(w[2], w[3], group_w8(m1));
 #pragma unroll
@@ -158,18 +174,21 @@ __global__ __launch_bounds__(kW8Waves * 64) void w8_stream_kernel(
 // WN*CT*32 columns over all of K.  Per chunk (64 of K) the workgroup copies
 // its BM x 64 bytes of X into one slot of a two-slot LDS ring (rows padded to
 // 80 bytes: the 16-byte operand reads of 16 consecutive rows then cover all
-// 64 banks once), while each wave turns its CT tiles' codes into int8 B
-// operands in registers (the next chunk's codes already in flight) and runs
-// RT x CT x 2 MFMAs with A operands read from LDS.  One barrier per chunk.
-// Tiles are ordered so that the workgroups resident on one XCD at a time
-// share rows of X and columns of W in that XCD's L2.
+// 64 banks once).  Each wave keeps its CT tiles' codes and group constants
+// PD chunks ahead in a register ring, and turns chunk c+1's codes into int8
+// B operands while the MFMAs of chunk c run (the two sets of operands are
+// independent, so the VALU work hides under the matrix pipe).  One barrier
+// per chunk.  Tiles are ordered so that the workgroups resident on one XCD at
+// a time share rows of X and columns of W in that XCD's L2.
 // ---------------------------------------------------------------------------
-template <int RT, int CT, int WM, int WN, bool G32, int OUT>
+template <int RT, int CT, int WM, int WN, int PD, int XD, bool G32, int OUT>
 __global__ __launch_bounds__(kW8Waves * 64) void w8_tiled_kernel(
     const int8_t* __restrict__ X, const float* __restrict__ sx, const uint8_t* __restrict__ blob,
     void* __restrict__ Y, int M, int N, int K, int gshift, size_t m_off, size_t c_off, int nbm,
     int nbn) {
     static_assert(WM * WN == kW8Waves, "eight waves");
+    static_assert(PD % 2 == 0 && kKAlign / kChunkK % PD == 0, "the ring divides the chunk count");
+    static_assert(XD == 1 || XD == 2, "X is loaded one or two chunks ahead");
     constexpr int BM = WM * RT * 32;
     constexpr int BN = WN * CT * 32;
     constexpr int RB = kTiledRowBytes;
@@ -236,50 +255,64 @@ __global__ __launch_bounds__(kW8Waves * 64) void w8_tiled_kernel(
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[r][j][i] = 0;
 
-    // prologue: X of chunk 0 into slot 0, codes of chunks 0 and 1 in flight
+    // ring slot s holds the codes and group constants of the chunk c with c % PD == s
+    u32x4 wb[PD][CT];
+    uint32_t mt[PD][CT][2];
+    auto fill = [&](int s, int c) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < CT; ++j) {
+            wb[s][j] = __builtin_nontemporal_load(wsrc[j] + (size_t)c * 64);
+            mt[s][j][0] = msrc[j][(size_t)group_of<G32>(c, 0, gshift) * 32];
+            mt[s][j][1] = G32 ? msrc[j][(size_t)group_of<G32>(c, 1, gshift) * 32] : 0u;
+        }
+    };
+    auto operands = [&](int s, i32x4 (&bq)[CT][2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < CT; ++j) {
+            const u32x4 w = wb[s][j];
+            bq[j][0] = operand_b(w[0], w[1], group_w8(mt[s][j][0]));
+            bq[j][1] = operand_b(w[2], w[3], group_w8(G32 ? mt[s][j][1] : mt[s][j][0]));
+        }
+    };
+
+    // prologue: X of chunk 0 into LDS slot 0, the ring filled, B of chunk 0 made
+    // X ring (XD = 2): xr[c % 2] receives chunk c + 2 while chunk c + 1 waits in the other
+    i32x4 xr[XD][PIECES];
     {
-        i32x4 xr[PIECES];
 #pragma unroll
-        for (int i = 0; i < PIECES; ++i) xr[i] = *(const i32x4*)xg[i];
+        for (int i = 0; i < PIECES; ++i) xr[0][i] = *(const i32x4*)xg[i];
+        if constexpr (XD == 2) {
 #pragma unroll
-        for (int i = 0; i < PIECES; ++i) *(i32x4*)(lds + xl[i]) = xr[i];
+            for (int i = 0; i < PIECES; ++i)
+                xr[1][i] = *(const i32x4*)(xg[i] + (size_t)min(1, KC - 1) * kChunkK);
+        }
+#pragma unroll
+        for (int s = 0; s < PD; ++s) fill(s, min(s, KC - 1));
+#pragma unroll
+        for (int i = 0; i < PIECES; ++i) *(i32x4*)(lds + xl[i]) = xr[0][i];
     }
-    u32x4 wb[2][CT];
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-        for (int j = 0; j < CT; ++j)
-            wb[q][j] = __builtin_nontemporal_load(wsrc[j] + (size_t)min(q, KC - 1) * 64);
+    i32x4 bqa[CT][2], bqb[CT][2];
+    operands(0, bqa);
+    fill(0, min(PD, KC - 1));
     __syncthreads();
 
-    for (int cb = 0; cb < KC; cb += 2) {   // KC is a multiple of 4
+    for (int cb = 0; cb < KC; cb += PD) {   // KC is a multiple of PD
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
+        for (int q = 0; q < PD; ++q) {
             const int c = cb + q;
-            const uint8_t* slot = lds + q * SLOT;   // chunk c lives in slot c % 2 == q
-            // X of chunk c+1 (clamped; the last one is a harmless repeat)
-            i32x4 xr[PIECES];
-            const int cn = min(c + 1, KC - 1);
+            // chunk c's B operands are in bqa (q even) or bqb (q odd); chunk c+1's go to the other
+            i32x4 (&cur)[CT][2] = (q & 1) ? bqb : bqa;
+            i32x4 (&nxt)[CT][2] = (q & 1) ? bqa : bqb;
+            const uint8_t* slot = lds + (q & 1) * SLOT;   // chunk c lives in LDS slot c % 2
+            // X of chunk c + XD (clamped; the last ones are harmless repeats)
+            i32x4 (&xin)[PIECES] = xr[XD == 2 ? (q & 1) : 0];
+            const int cn = min(c + XD, KC - 1);
 #pragma unroll
-            for (int i = 0; i < PIECES; ++i) xr[i] = *(const i32x4*)(xg[i] + (size_t)cn * kChunkK);
-            // group constants of chunk c
-            uint32_t mt[CT][2];
-#pragma unroll
-            for (int j = 0; j < CT; ++j) {
-                mt[j][0] = msrc[j][(size_t)group_of<G32>(c, 0, gshift) * 32];
-                mt[j][1] = G32 ? msrc[j][(size_t)group_of<G32>(c, 1, gshift) * 32] : mt[j][0];
-            }
-            // B operands of chunk c, then the codes of chunk c+2 into the freed registers
-            i32x4 bq[CT][2];
-#pragma unroll
-            for (int j = 0; j < CT; ++j) {
-                const u32x4 w = wb[q][j];
-                bq[j][0] = operand_b(w[0], w[1], group_w8(mt[j][0]));
-                bq[j][1] = operand_b(w[2], w[3], group_w8(mt[j][1]));
-            }
-#pragma unroll
-            for (int j = 0; j < CT; ++j)
-                wb[q][j] = __builtin_nontemporal_load(wsrc[j] + (size_t)min(c + 2, KC - 1) * 64);
+            for (int i = 0; i < PIECES; ++i) xin[i] = *(const i32x4*)(xg[i] + (size_t)cn * kChunkK);
+            // B of chunk c+1, then its ring slot refilled with chunk c+1+PD
+            const int sn = (q + 1) % PD;
+            operands(sn, nxt);
+            fill(sn, min(c + 1 + PD, KC - 1));
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
                 i32x4 a[RT];
@@ -290,13 +323,14 @@ __global__ __launch_bounds__(kW8Waves * 64) void w8_tiled_kernel(
                 for (int r = 0; r < RT; ++r)
 #pragma unroll
                     for (int j = 0; j < CT; ++j)
-                        acc[r][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[r], bq[j][s],
+                        acc[r][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[r], cur[j][s],
                                                                           acc[r][j], 0, 0, 0);
             }
-            // slot (c+1) % 2 was last read in chunk c-1, before the previous barrier
-            uint8_t* next = lds + (1 - q) * SLOT;
+            // LDS slot (c+1) % 2 was last read in chunk c-1, before the previous barrier
+            uint8_t* next = lds + (1 - (q & 1)) * SLOT;
+            i32x4 (&xout)[PIECES] = xr[XD == 2 ? 1 - (q & 1) : 0];   // chunk c + 1
 #pragma unroll
-            for (int i = 0; i < PIECES; ++i) *(i32x4*)(next + xl[i]) = xr[i];
+            for (int i = 0; i < PIECES; ++i) *(i32x4*)(next + xl[i]) = xout[i];
             __syncthreads();
         }
     }
@@ -348,15 +382,20 @@ hipError_t launch_g(const int8_t* xq, const float* sx, const void* packed, void*
         return launch_stream_kp<2, G32>(xq, sx, packed, Y, M, L, plan, gshift, stream);
     }
     if (plan.cfg == 0)
-        w8_tiled_kernel<4, 2, 2, 4, G32, W4A8_TU_OUT><<<plan.grid, kW8Waves * 64, plan.lds,
-                                                        stream>>>(
-            xq, sx, b, Y, (int)M, (int)L.N, (int)L.K, gshift, L.m_off, L.c_off, plan.nbm,
-            plan.nbn);
+        w8_tiled_kernel<4, 2, 2, 4, 2, (G32 ? 1 : 2), G32, W4A8_TU_OUT>
+            <<<plan.grid, kW8Waves * 64, plan.lds, stream>>>(xq, sx, b, Y, (int)M, (int)L.N,
+                                                             (int)L.K, gshift, L.m_off, L.c_off,
+                                                             plan.nbm, plan.nbn);
+    else if (plan.cfg == 1)
+        w8_tiled_kernel<2, 1, 2, 4, 4, 2, G32, W4A8_TU_OUT>
+            <<<plan.grid, kW8Waves * 64, plan.lds, stream>>>(xq, sx, b, Y, (int)M, (int)L.N,
+                                                             (int)L.K, gshift, L.m_off, L.c_off,
+                                                             plan.nbm, plan.nbn);
     else
-        w8_tiled_kernel<2, 1, 2, 4, G32, W4A8_TU_OUT><<<plan.grid, kW8Waves * 64, plan.lds,
-                                                        stream>>>(
-            xq, sx, b, Y, (int)M, (int)L.N, (int)L.K, gshift, L.m_off, L.c_off, plan.nbm,
-            plan.nbn);
+        w8_tiled_kernel<4, 1, 2, 4, 4, 2, G32, W4A8_TU_OUT>
+            <<<plan.grid, kW8Waves * 64, plan.lds, stream>>>(xq, sx, b, Y, (int)M, (int)L.N,
+                                                             (int)L.K, gshift, L.m_off, L.c_off,
+                                                             plan.nbm, plan.nbn);
     return hipGetLastError();
 }
 

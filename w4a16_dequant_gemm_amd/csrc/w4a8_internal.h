@@ -73,23 +73,24 @@ inline LayoutW8 make_layout_w8(int64_t K, int64_t N, int64_t G) {
 enum { OUT_F16 = 0, OUT_BF16 = 1, OUT_I32 = 2 };
 
 // Kernel variants.
-//   STREAM: M <= 64.  Eight waves per workgroup = (8/KP) tiles x KP parts of
-//           K; each wave streams its tile's chunks and reads its rows of X
+//   STREAM: M <= 32 (up to 64 when asked for).  Eight waves per workgroup =
+//           (8/KP) tiles x KP parts of K; each wave streams its tile's chunks and reads its rows of X
 //           straight from memory (X is small and stays in L2); the parts meet
 //           in LDS (integer sums, so their order does not matter).
-//   TILED:  M > 64.  Eight waves = WM x WN; a workgroup owns BM rows x BN
+//   TILED:  M > 32.  Eight waves = WM x WN; a workgroup owns BM rows x BN
 //           columns over all of K; X goes through a two-slot LDS ring, each
 //           wave streams its own tiles' weights.
 enum VariantW8 { W8_STREAM = 0, W8_TILED = 1 };
 constexpr int kW8Waves = 8;
-constexpr int kStreamMaxRows = 64;
+constexpr int kStreamMaxRows = 64;      // largest M the streaming kernel takes
+constexpr int kStreamDefaultRows = 32;  // largest M it is chosen for by default
 constexpr int kTiledRowBytes = 80;   // 64 bytes of X per row and chunk + 16 of padding
 
 struct PlanW8 {
     VariantW8 variant;
     int rt;          // 32-row tiles per wave
     int kp;          // STREAM: parts of K per tile
-    int cfg;         // TILED: 0 = 256 x 256 workgroup tile, 1 = 128 x 128
+    int cfg;         // TILED: workgroup tile 0 = 256 x 256, 1 = 128 x 128, 2 = 256 x 128
     int grid;        // workgroups
     int nbm, nbn;    // TILED: row and column blocks
     size_t lds;      // dynamic LDS bytes
