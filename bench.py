@@ -28,6 +28,7 @@ import w4a16_synth as synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
 MFMA_PEAK_TFLOPS = 2500.0    # MI355X dense fp16/bf16 MFMA, 2.5 PFLOP/s
+INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA, 5.0 POP/s
 DEFAULT_WORKLOAD = "decode_m1_k8192_n28672_fp16_asym_g128_outliers"
 METRIC = "W4A16 GEMM achieved HBM GB/s"
 
@@ -129,23 +130,24 @@ def cpu_baseline(name, cfg, budget_s=12.0):
 KERNEL_SOURCES = ("w4a16_gemm.hip", "w4a16_decode.hip", "w4a16_wide.hip", "w4a16_device.h",
                   "w4a16_epilogue.h",
                   "w4a16_layout.h", "w4a16_internal.h", "w4a16_api.cpp")
+KERNEL_SOURCES_W4A8 = ("w4a8_gemm.hip", "w4a8_device.h", "w4a8_internal.h", "w4a8_api.cpp")
 # Reported beside the headline workload (same protocol, no CPU baseline or
 # comparators): the prefill and the batched shapes of the same layer.
 EXTRA_WORKLOADS = ("prefill_m4096_k8192_n28672_bf16_asym_g128",
                    "batch_m64_k8192_n28672_fp16_asym_g64")
 
 
-def kernel_source_hash():
+def kernel_source_hash(sources=KERNEL_SOURCES):
     import hashlib
 
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in sources:
         with open(os.path.join(ROOT, "w4a16_dequant_gemm_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(name):
+def measured_traffic(name, sources=KERNEL_SOURCES):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
     record of this workload, or None if there is none or the kernel sources
     changed since it was taken."""
@@ -154,7 +156,7 @@ def measured_traffic(name):
         return None
     with open(path) as fh:
         rec = json.load(fh).get(name)
-    if not rec or rec.get("source_hash") != kernel_source_hash():
+    if not rec or rec.get("source_hash") != kernel_source_hash(sources):
         return None
     return int(rec["traffic_bytes"])
 
@@ -309,6 +311,91 @@ def run_workload(name, steps, warmup, rotate_bytes=1 << 30, with_cpu=True, compa
     return out
 
 
+def w8_bytes(cfg):
+    """Algorithmic bytes of one W4A8 call: the blob (codes, group constants,
+    column scales), the int8 activations and their row scales, the fp16 output."""
+    M, K, N, G = cfg["M"], cfg["K"], cfg["N"], cfg["G"]
+    return K * N // 2 + (K // G) * N * 2 + N * 4 + M * K + M * 4 + M * N * 2
+
+
+def run_workload_w8(name, steps, warmup, rotate_bytes=1 << 30):
+    """One W4A8 workload (w4a8_gemm, fp16 output) with the protocol of
+    run_workload: cold weight copies, `steps` calls in one HIP graph between
+    two events, then per-launch event pairs."""
+    import torch
+
+    import w4a16_dequant_gemm_amd as w4
+    from w4a16_dequant_gemm_amd import w4a8 as w8
+
+    w4.load_library()
+    cfg = dict(synth.W4A8_WORKLOADS[name])
+    M, K, N, G = cfg["M"], cfg["K"], cfg["N"], cfg["G"]
+    dev = torch.device("cuda:0")
+    p = synth.make_w4a8_problem(seed=0, **cfg)
+    xq = torch.from_numpy(p.xq).to(dev)
+    sx = torch.from_numpy(p.sx).to(dev)
+    base = w8.w4a8_repack(torch.from_numpy(p.qweight.view(np.int32)).to(dev),
+                          torch.from_numpy(p.s8).to(dev), torch.from_numpy(p.a).to(dev),
+                          torch.from_numpy(p.sw).to(dev), K, N, G)
+    copies = max(2, min(16, math.ceil(rotate_bytes / base.data.numel())))
+    blobs = [base] + [w8.PackedW8(base.data.clone(), K, N, G) for _ in range(copies - 1)]
+    Y = torch.empty((M, N), dtype=torch.float16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        w8.w4a8_gemm(xq, sx, blobs[i % copies], out="fp16", Y=Y)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(steps):
+            step(i)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    graph.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / steps
+    del graph
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    hold_gpu(5.0 + 0.1 * steps)
+    for i in range(steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    per_launch = np.array([a.elapsed_time(b) for a, b in ev])
+    nbytes = w8_bytes(cfg)
+    ops = 2 * M * N * K
+    gbs = nbytes / (ms_step * 1e-3) / 1e9
+    tops = ops / (ms_step * 1e-3) / 1e12
+    # ridge of the int8 roofline: 5.0e15 / 8e12 = 625 op/byte
+    if ops / nbytes > INT8_PEAK_TOPS / HBM_PEAK_GBS * 1e3:
+        roof = {"bound": "mfma", "achieved": round(tops, 1), "peak": INT8_PEAK_TOPS,
+                "unit": "TOP/s (int8)", "frac": round(tops / INT8_PEAK_TOPS, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    roof["traffic"] = measured_traffic(name, KERNEL_SOURCES_W4A8)
+    return {
+        "ms_per_step": round(ms_step, 5), "steps": steps, "kernel_us": round(ms_step * 1e3, 3),
+        "kernel_us_event_pairs_mean_p50": [round(float(np.mean(per_launch)) * 1e3, 3),
+                                           round(float(np.median(per_launch)) * 1e3, 3)],
+        "gbs": round(gbs, 1), "tops_int8": round(tops, 1), "algorithmic_bytes": nbytes,
+        "roofline": roof, "kernel_source_hash": kernel_source_hash(KERNEL_SOURCES_W4A8),
+        "config": {"workload": name, "M": M, "K": K, "N": N, "group_size": G,
+                   "act": "int8 per row", "out": "fp16", "cold_weight_copies": copies,
+                   "launch": "hip_graph_replay"},
+    }
+
+
 def comparator_times(p, X, blobs, copies, stream, reps=20):
     """Context, not the metric: a dense fp16/bf16 torch.matmul (hipBLASLt) on the
     same shape, and the unfused route (dequantize to HBM, then torch.matmul)."""
@@ -451,7 +538,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
-                    help="a name from w4a16_synth.WORKLOADS, 'all' (one line each), or "
+                    help="a name from w4a16_synth.WORKLOADS or W4A8_WORKLOADS, 'all' (one "
+                         "line each), or "
                          "one of " + ", ".join(LAYER_WORKLOADS) + " (fused FFN block)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-comparators", action="store_true")
@@ -488,12 +576,23 @@ def main():
         name_, _, param = args.plan.partition(":")
         plan = (name_, int(param or 0))
     names = list(synth.WORKLOADS) if args.workload == "all" else args.workload.split(",")
+    if all(n in synth.W4A8_WORKLOADS for n in names):
+        for name in names:
+            out = run_workload_w8(name, args.steps, args.warmup)
+            out.update({"metric": "W4A8 GEMM achieved " + out["roofline"]["unit"],
+                        "value": out["roofline"]["achieved"], "unit": out["roofline"]["unit"],
+                        "n_gpus": 1, "warmup": args.warmup, "higher_is_better": True,
+                        "scaling": "weak", "vs_baseline": None, "dtype": "i8",
+                        "data": "synthetic"})
+            print(json.dumps(out), flush=True)
+        return
     for name in names:
         out = run_workload(name, args.steps, args.warmup,
                            with_cpu=not args.no_cpu and len(names) == 1,
                            comparators=not args.no_comparators, plan=plan, rows=args.m)
         if len(names) == 1 and not args.no_extra and plan is None and args.m is None:
             out["extra_workloads"] = extra_workloads(name, min(args.steps, 50), min(args.warmup, 5))
+            out["w4a8_workloads"] = w4a8_workloads(min(args.steps, 50), min(args.warmup, 5))
         print(json.dumps(out), flush=True)
 
 
@@ -511,6 +610,20 @@ def extra_workloads(headline, steps, warmup):
                                        "read_probe_gbs", "tflops", "algorithmic_bytes")}
         res[name]["config"] = {k: o["config"][k] for k in ("M", "K", "N", "group_size",
                                                            "act_dtype", "quant")}
+        torch.cuda.empty_cache()
+    return res
+
+
+def w4a8_workloads(steps, warmup):
+    """The W4A8 route on its workloads (decode, batch 128, prefill), measured
+    with the same protocol in the same process."""
+    import torch
+
+    res = {}
+    for name in synth.W4A8_WORKLOADS:
+        o = run_workload_w8(name, steps, warmup)
+        res[name] = {k: o[k] for k in ("kernel_us", "ms_per_step", "steps", "roofline", "gbs",
+                                       "tops_int8", "algorithmic_bytes")}
         torch.cuda.empty_cache()
     return res
 
