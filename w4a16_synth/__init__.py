@@ -34,7 +34,9 @@ import numpy as np
 
 __all__ = ["Problem", "make_problem", "make_weights", "make_activations", "with_activations",
            "pack_nibbles", "to_dtype_bits", "WORKLOADS", "workload", "ProblemW8",
-           "make_w4a8_weights", "make_w4a8_activations", "make_w4a8_problem", "W4A8_WORKLOADS"]
+           "make_w4a8_weights", "make_w4a8_activations", "make_w4a8_problem", "W4A8_WORKLOADS",
+           "ProblemMX", "make_mxfp4_weights", "make_mx_activations", "make_mxfp4_problem",
+           "MXFP4_WORKLOADS"]
 
 
 def to_dtype_bits(x64: np.ndarray, dtype: str) -> np.ndarray:
@@ -209,4 +211,54 @@ W4A8_WORKLOADS = {
     "w4a8_decode_m1_k8192_n28672_g128": dict(M=1, K=8192, N=28672, G=128),
     "w4a8_batch_m128_k8192_n28672_g128": dict(M=128, K=8192, N=28672, G=128),
     "w4a8_prefill_m4096_k8192_n28672_g128": dict(M=4096, K=8192, N=28672, G=128),
+}
+
+
+# ---------------------------------------------------------------------------
+# MXFP4 route inputs.  Random draws only:
+#   q    uint8 [K][N] E2M1 codes, uniform 0..15, packed like qweight (stream 1)
+#   ws   uint8 [K/32][N] E8M0 weight block scales, uniform in [118, 124] (stream 2)
+#   xq   uint8 [M][K] E4M3 codes, uniform over the 254 finite codes (stream 0)
+#   xs   uint8 [M][K/32] E8M0 activation block scales, uniform in [116, 122] (stream 4)
+# (activations taken from real values go through the quantiser instead)
+# ---------------------------------------------------------------------------
+
+@dataclass
+class ProblemMX:
+    M: int
+    K: int
+    N: int
+    xq: np.ndarray       # uint8 [M][K]
+    xs: np.ndarray       # uint8 [M][K/32]
+    qweight: np.ndarray  # uint32 [K/8][N]
+    ws: np.ndarray       # uint8 [K/32][N]
+
+
+def make_mxfp4_weights(K: int, N: int, seed: int = 0):
+    if K % 32:
+        raise ValueError("K must be a multiple of 32")
+    st = _streams(seed)
+    q = st[1].integers(0, 16, size=(K, N), dtype=np.uint8)
+    ws = st[2].integers(118, 125, size=(K // 32, N), dtype=np.int64).astype(np.uint8)
+    return pack_nibbles(q), ws
+
+
+def make_mx_activations(M: int, K: int, seed: int = 0):
+    st = _streams(seed)
+    c = st[0].integers(0, 254, size=(M, K), dtype=np.int64)
+    xq = np.where(c >= 127, c + 1, c).astype(np.uint8)      # skip 0x7F (NaN); 0xFF is never drawn
+    xs = st[4].integers(116, 123, size=(M, K // 32), dtype=np.int64).astype(np.uint8)
+    return xq, xs
+
+
+def make_mxfp4_problem(M: int, K: int, N: int, seed: int = 0) -> ProblemMX:
+    qweight, ws = make_mxfp4_weights(K, N, seed)
+    xq, xs = make_mx_activations(M, K, seed)
+    return ProblemMX(M, K, N, xq, xs, qweight, ws)
+
+
+MXFP4_WORKLOADS = {
+    "mxfp4_decode_m1_k8192_n28672": dict(M=1, K=8192, N=28672),
+    "mxfp4_batch_m128_k8192_n28672": dict(M=128, K=8192, N=28672),
+    "mxfp4_prefill_m4096_k8192_n28672": dict(M=4096, K=8192, N=28672),
 }
