@@ -11,7 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libw4a16.so")
 HEADERS = ["w4a16_layout.h", "w4a16_device.h", "w4a16_internal.h", "w4a16_epilogue.h",
-           "w4a8_internal.h", "w4a8_device.h"]
+           "w4a8_internal.h", "w4a8_device.h", "mx_internal.h"]
 
 COMMON = [
     "--offload-arch=gfx950",
@@ -47,6 +47,10 @@ UNITS = [
     ("w4a8_gemm.hip", ["-DW4A8_TU_OUT=0"]),
     ("w4a8_gemm.hip", ["-DW4A8_TU_OUT=1"]),
     ("w4a8_gemm.hip", ["-DW4A8_TU_OUT=2"]),
+    ("mx_api.cpp", []),
+    ("mx_prep.hip", []),
+    ("mx_gemm.hip", ["-DMXFP4_TU_BF16=0"]),
+    ("mx_gemm.hip", ["-DMXFP4_TU_BF16=1"]),
 ]
 
 

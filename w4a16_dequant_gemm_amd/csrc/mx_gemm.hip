@@ -1,0 +1,388 @@
+// mx_gemm.hip -- the MXFP4 GEMM kernels for gfx950: E2M1 weight codes and
+// E4M3 activations go straight into v_mfma_scale_f32_32x32x64_f8f6f4 with
+// their E8M0 block scales (one scale byte per lane and operand), fp32
+// accumulation, one rounding to the output dtype.
+//
+// Page "量化开销对比" (laojiahuo2003.github.io), section 3, closing paragraph
+// (hardware block scales of 32 bring 4-bit weights back to route A: no
+// dequantisation in the kernel) and section 1 (route A).  The operand layouts
+// are described in mx_internal.h.
+//
+// Compiled once per output dtype (MXFP4_TU_BF16 = 0 fp16, 1 bf16).
+#include <hip/hip_runtime.h>
+
+#include "mx_internal.h"
+
+#ifndef MXFP4_TU_BF16
+#define MXFP4_TU_BF16 0
+#endif
+
+namespace mxfp4 {
+
+namespace {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int acc_row(int r, int lane) {
+    return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store_out(void* Y, int64_t idx, float v) {
+    uint16_t b;
+    if constexpr (BF16)
+        b = __builtin_bit_cast(uint16_t, (__bf16)v);
+    else
+        b = __builtin_bit_cast(uint16_t, (_Float16)v);
+    ((uint16_t*)Y)[idx] = b;
+}
+
+// A operand (32 E4M3 bytes) from its two 16-byte halves; B operand (32 E2M1
+// codes in 16 bytes, the upper half unused).
+__device__ __forceinline__ i32x8 cat(i32x4 lo, i32x4 hi) {
+    i32x8 r;
+    r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+    r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+    return r;
+}
+
+__device__ __forceinline__ i32x8 widen(u32x4 w) {
+    i32x8 r;
+    r[0] = (int)w[0]; r[1] = (int)w[1]; r[2] = (int)w[2]; r[3] = (int)w[3];
+    r[4] = 0; r[5] = 0; r[6] = 0; r[7] = 0;
+    return r;
+}
+
+__device__ __forceinline__ f32x16 mma(i32x8 a, i32x8 b, f32x16 c, int sa, int sb) {
+    // A: E4M3 (format 0), B: E2M1 (format 4); scale bytes in bits 0..7
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 4, 0, sa, 0, sb);
+}
+
+// ---------------------------------------------------------------------------
+// Streaming kernel (M <= 64).  Wave w of a workgroup works on tile
+// blockIdx.x * (8/KP) + w / KP over part w % KP of the k-steps; per k-step a
+// lane needs 16 bytes of codes, the tile's scale byte, 2 x 16 bytes of X per
+// row tile and its row's scale byte, all in a ring of P k-steps in flight.
+// The KP parts of a tile add up in LDS in part order.
+// ---------------------------------------------------------------------------
+constexpr int kStreamDepth = 4;
+
+template <int RT, int KP, bool BF16>
+__global__ __launch_bounds__(kMxWaves * 64) void mx_stream_kernel(
+    const uint8_t* __restrict__ X, const uint8_t* __restrict__ XS, const uint8_t* __restrict__ blob,
+    void* __restrict__ Y, int M, int N, int K, size_t s_off) {
+    constexpr int CTW = kMxWaves / KP;
+    constexpr int P = kStreamDepth;
+    extern __shared__ float red[];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int part = wave % KP;
+    const int ctl = wave / KP;
+    const int KS = K / kStepK;
+    const int KQ = K / kKAlign;
+    const int t = blockIdx.x * CTW + ctl;
+    const int per = (KS + KP - 1) / KP;
+    const int c0 = min(part * per, KS);
+    const int c1 = min(c0 + per, KS);
+    const int n = c1 - c0;
+    const int h = lane >> 5;
+
+    const u32x4* wsrc = (const u32x4*)blob + (size_t)t * KS * 64 + lane;
+    const uint8_t* ssrc = blob + s_off + (size_t)t * KQ * 256 + lane * 4;
+    const uint8_t* xsrc[RT];
+    const uint8_t* xssrc[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+        const int row = min(32 * r + (lane & 31), M - 1);
+        xsrc[r] = X + (size_t)row * K + 16 * h;
+        xssrc[r] = XS + (size_t)row * (K / 32) + h;
+    }
+
+    f32x16 acc[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[r][i] = 0.0f;
+
+    u32x4 wb[P];
+    uint32_t sbw[P];
+    i32x4 xb[P][RT][2];
+    uint32_t sab[P][RT];
+    auto fill = [&](int i, int c) __attribute__((always_inline)) {
+        wb[i] = __builtin_nontemporal_load(wsrc + (size_t)c * 64);
+        sbw[i] = ssrc[(size_t)(c >> 2) * 256 + (c & 3)];
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            xb[i][r][0] = *(const i32x4*)(xsrc[r] + (size_t)c * kStepK);
+            xb[i][r][1] = *(const i32x4*)(xsrc[r] + (size_t)c * kStepK + 32);
+            sab[i][r] = xssrc[r][2 * c];
+        }
+    };
+#pragma unroll
+    for (int i = 0; i < P; ++i) fill(i, min(c0 + i, c1 - 1));
+
+    for (int base = 0; base < n; base += P) {
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+            const int c = c0 + base + i;
+            if (base + i < n) {
+                const i32x8 b = widen(wb[i]);
+                const int sb = (int)sbw[i];
+                i32x8 a[RT];
+                int sa[RT];
+#pragma unroll
+                for (int r = 0; r < RT; ++r) {
+                    a[r] = cat(xb[i][r][0], xb[i][r][1]);
+                    sa[r] = (int)sab[i][r];
+                }
+                fill(i, min(c + P, c1 - 1));
+#pragma unroll
+                for (int r = 0; r < RT; ++r) acc[r] = mma(a[r], b, acc[r], sa[r], sb);
+            }
+        }
+    }
+
+    if constexpr (KP > 1) {
+        if (part > 0) {
+#pragma unroll
+            for (int r = 0; r < RT; ++r)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    red[((((part - 1) * CTW + ctl) * RT + r) * 16 + i) * 64 + lane] = acc[r][i];
+        }
+        __syncthreads();
+        if (part > 0) return;
+#pragma unroll 1
+        for (int p = 1; p < KP; ++p)
+#pragma unroll
+            for (int r = 0; r < RT; ++r)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    acc[r][i] += red[((((p - 1) * CTW + ctl) * RT + r) * 16 + i) * 64 + lane];
+    }
+
+    const int col = t * kTileCols + (lane & 31);
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int row = 32 * r + acc_row(i, lane);
+            if (row < M) store_out<BF16>(Y, (int64_t)row * N + col, acc[r][i]);
+        }
+}
+
+// ---------------------------------------------------------------------------
+// Tiled kernel (M > 32).  A workgroup owns BM = WM*RT*32 rows and BN =
+// WN*CT*32 columns over all of K.  X goes through a two-slot LDS ring (rows of
+// 64 bytes per k-step padded to 80, loaded two k-steps ahead), each wave's
+// codes and scale bytes through a register ring PD k-steps deep; the scale
+// bytes of X rows come straight from memory with the codes.  One barrier per
+// k-step; the XCD-grouped tile order of the W4A8 tiled kernel.
+// ---------------------------------------------------------------------------
+template <int RT, int CT, int WM, int WN, int PD, bool BF16>
+__global__ __launch_bounds__(kMxWaves * 64) void mx_tiled_kernel(
+    const uint8_t* __restrict__ X, const uint8_t* __restrict__ XS, const uint8_t* __restrict__ blob,
+    void* __restrict__ Y, int M, int N, int K, size_t s_off, int nbm, int nbn) {
+    static_assert(WM * WN == kMxWaves, "eight waves");
+    static_assert(PD % 2 == 0 && kKAlign / kStepK % PD == 0, "the ring divides the k-steps");
+    constexpr int BM = WM * RT * 32;
+    constexpr int BN = WN * CT * 32;
+    constexpr int RB = kMxRowBytes;
+    constexpr int SLOT = BM * RB;
+    constexpr int PIECES = BM * 4 / (kMxWaves * 64);
+    static_assert(PIECES >= 1 && BM * 4 == PIECES * kMxWaves * 64, "X staging");
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave / WN;
+    const int wn = wave % WN;
+    const int KS = K / kStepK;
+    const int KQ = K / kKAlign;
+    const int NT = N / kTileCols;
+    const int h = lane >> 5;
+
+    const int T = nbm * nbn;
+    int task = blockIdx.x;
+    if (T % 8 == 0) task = (blockIdx.x % 8) * (T / 8) + blockIdx.x / 8;
+    constexpr int GM = 4;
+    const int group = task / (GM * nbn);
+    const int first_m = group * GM;
+    const int gsz = min(nbm - first_m, GM);
+    const int in_group = task % (GM * nbn);
+    const int mb = first_m + in_group % gsz;
+    const int nb = in_group / gsz;
+    const int m0 = mb * BM;
+
+    int tile[CT];
+    bool tile_ok[CT];
+    const u32x4* wsrc[CT];
+    const uint8_t* ssrc[CT];
+#pragma unroll
+    for (int j = 0; j < CT; ++j) {
+        const int tt = nb * (BN / 32) + wn * CT + j;
+        tile_ok[j] = tt < NT;
+        tile[j] = min(tt, NT - 1);
+        wsrc[j] = (const u32x4*)blob + (size_t)tile[j] * KS * 64 + lane;
+        ssrc[j] = blob + s_off + (size_t)tile[j] * KQ * 256 + lane * 4;
+    }
+    const uint8_t* xssrc[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+        xssrc[r] = XS + (size_t)min(m0 + wm * RT * 32 + 32 * r + (lane & 31), M - 1) * (K / 32) + h;
+
+    const uint8_t* xg[PIECES];
+    int xl[PIECES];
+#pragma unroll
+    for (int i = 0; i < PIECES; ++i) {
+        const int p = tid + kMxWaves * 64 * i;
+        const int row = p >> 2;
+        xg[i] = X + (size_t)min(m0 + row, M - 1) * K + 16 * (p & 3);
+        xl[i] = row * RB + 16 * (p & 3);
+    }
+    const int arow = (wm * RT * 32 + (lane & 31)) * RB + 16 * h;
+
+    f32x16 acc[RT][CT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int j = 0; j < CT; ++j)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[r][j][i] = 0.0f;
+
+    // ring slot s: codes, B scale bytes and X scale bytes of the k-step c with c % PD == s
+    u32x4 wb[PD][CT];
+    uint32_t sbw[PD][CT];
+    uint32_t sab[PD][RT];
+    auto fill = [&](int s, int c) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < CT; ++j) {
+            wb[s][j] = __builtin_nontemporal_load(wsrc[j] + (size_t)c * 64);
+            sbw[s][j] = ssrc[j][(size_t)(c >> 2) * 256 + (c & 3)];
+        }
+#pragma unroll
+        for (int r = 0; r < RT; ++r) sab[s][r] = xssrc[r][2 * c];
+    };
+
+    // X two k-steps ahead: xr[c % 2] receives k-step c + 2 while c + 1 waits in the other
+    i32x4 xr[2][PIECES];
+#pragma unroll
+    for (int i = 0; i < PIECES; ++i) {
+        xr[0][i] = *(const i32x4*)xg[i];
+        xr[1][i] = *(const i32x4*)(xg[i] + (size_t)min(1, KS - 1) * kStepK);
+    }
+#pragma unroll
+    for (int s = 0; s < PD; ++s) fill(s, min(s, KS - 1));
+#pragma unroll
+    for (int i = 0; i < PIECES; ++i) *(i32x4*)(lds + xl[i]) = xr[0][i];
+    __syncthreads();
+
+    for (int cb = 0; cb < KS; cb += PD) {   // KS is a multiple of PD
+#pragma unroll
+        for (int q = 0; q < PD; ++q) {
+            const int c = cb + q;
+            const uint8_t* slot = lds + (q & 1) * SLOT;   // k-step c lives in LDS slot c % 2
+            i32x4 (&xin)[PIECES] = xr[q & 1];
+            const int cn = min(c + 2, KS - 1);
+#pragma unroll
+            for (int i = 0; i < PIECES; ++i) xin[i] = *(const i32x4*)(xg[i] + (size_t)cn * kStepK);
+            i32x8 b[CT];
+            int sb[CT];
+#pragma unroll
+            for (int j = 0; j < CT; ++j) {
+                b[j] = widen(wb[q][j]);
+                sb[j] = (int)sbw[q][j];
+            }
+            int sa[RT];
+#pragma unroll
+            for (int r = 0; r < RT; ++r) sa[r] = (int)sab[q][r];
+            fill(q, min(c + PD, KS - 1));
+#pragma unroll
+            for (int r = 0; r < RT; ++r) {
+                const i32x8 a = cat(*(const i32x4*)(slot + arow + r * 32 * RB),
+                                    *(const i32x4*)(slot + arow + r * 32 * RB + 32));
+#pragma unroll
+                for (int j = 0; j < CT; ++j) acc[r][j] = mma(a, b[j], acc[r][j], sa[r], sb[j]);
+            }
+            // LDS slot (c+1) % 2 was last read in k-step c-1, before the previous barrier
+            uint8_t* next = lds + (1 - (q & 1)) * SLOT;
+            i32x4 (&xout)[PIECES] = xr[1 - (q & 1)];   // k-step c + 1
+#pragma unroll
+            for (int i = 0; i < PIECES; ++i) *(i32x4*)(next + xl[i]) = xout[i];
+            __syncthreads();
+        }
+    }
+
+#pragma unroll
+    for (int j = 0; j < CT; ++j) {
+        if (!tile_ok[j]) continue;
+        const int col = tile[j] * kTileCols + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int row = m0 + wm * RT * 32 + 32 * r + acc_row(i, lane);
+                if (row < M) store_out<BF16>(Y, (int64_t)row * N + col, acc[r][j][i]);
+            }
+    }
+}
+
+template <int RT, int KP>
+hipError_t launch_stream_t(const uint8_t* xq, const uint8_t* xs, const void* packed, void* Y,
+                           int64_t M, const LayoutMX& L, const PlanMX& plan, hipStream_t stream) {
+    mx_stream_kernel<RT, KP, MXFP4_TU_BF16 != 0><<<plan.grid, kMxWaves * 64, plan.lds, stream>>>(
+        xq, xs, (const uint8_t*)packed, Y, (int)M, (int)L.N, (int)L.K, L.s_off);
+    return hipGetLastError();
+}
+
+template <int RT>
+hipError_t launch_stream_kp(const uint8_t* xq, const uint8_t* xs, const void* packed, void* Y,
+                            int64_t M, const LayoutMX& L, const PlanMX& plan, hipStream_t stream) {
+    switch (plan.kp) {
+        case 2: return launch_stream_t<RT, 2>(xq, xs, packed, Y, M, L, plan, stream);
+        case 4: return launch_stream_t<RT, 4>(xq, xs, packed, Y, M, L, plan, stream);
+        default: return launch_stream_t<RT, 8>(xq, xs, packed, Y, M, L, plan, stream);
+    }
+}
+
+hipError_t launch_part(const uint8_t* xq, const uint8_t* xs, const void* packed, void* Y,
+                       int64_t M, const LayoutMX& L, const PlanMX& plan, hipStream_t stream) {
+    constexpr bool BF = MXFP4_TU_BF16 != 0;
+    const uint8_t* b = (const uint8_t*)packed;
+    if (plan.variant == MX_STREAM) {
+        if (plan.rt == 1) return launch_stream_kp<1>(xq, xs, packed, Y, M, L, plan, stream);
+        return launch_stream_kp<2>(xq, xs, packed, Y, M, L, plan, stream);
+    }
+    if (plan.cfg == 0)
+        mx_tiled_kernel<4, 2, 2, 4, 2, BF><<<plan.grid, kMxWaves * 64, plan.lds, stream>>>(
+            xq, xs, b, Y, (int)M, (int)L.N, (int)L.K, L.s_off, plan.nbm, plan.nbn);
+    else if (plan.cfg == 1)
+        mx_tiled_kernel<2, 1, 2, 4, 4, BF><<<plan.grid, kMxWaves * 64, plan.lds, stream>>>(
+            xq, xs, b, Y, (int)M, (int)L.N, (int)L.K, L.s_off, plan.nbm, plan.nbn);
+    else
+        mx_tiled_kernel<4, 1, 2, 4, 4, BF><<<plan.grid, kMxWaves * 64, plan.lds, stream>>>(
+            xq, xs, b, Y, (int)M, (int)L.N, (int)L.K, L.s_off, plan.nbm, plan.nbn);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+#if MXFP4_TU_BF16
+hipError_t launch_mx_gemm_bf16(const uint8_t* xq, const uint8_t* xs, const void* packed, void* Y,
+                               int64_t M, const LayoutMX& L, const PlanMX& plan,
+                               hipStream_t stream) {
+    return launch_part(xq, xs, packed, Y, M, L, plan, stream);
+}
+#else
+hipError_t launch_mx_gemm_f16(const uint8_t* xq, const uint8_t* xs, const void* packed, void* Y,
+                              int64_t M, const LayoutMX& L, const PlanMX& plan,
+                              hipStream_t stream) {
+    return launch_part(xq, xs, packed, Y, M, L, plan, stream);
+}
+#endif
+
+}  // namespace mxfp4
