@@ -29,6 +29,7 @@ import w4a16_synth as synth  # noqa: E402
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
 MFMA_PEAK_TFLOPS = 2500.0    # MI355X dense fp16/bf16 MFMA, 2.5 PFLOP/s
 INT8_PEAK_TOPS = 5000.0      # MI355X dense int8 MFMA, 5.0 POP/s
+FP8_PEAK_TFLOPS = 5000.0     # MI355X dense fp8 MFMA, 5.0 PFLOP/s (the MXFP4 route's A operand is fp8)
 DEFAULT_WORKLOAD = "decode_m1_k8192_n28672_fp16_asym_g128_outliers"
 METRIC = "W4A16 GEMM achieved HBM GB/s"
 
@@ -131,6 +132,7 @@ KERNEL_SOURCES = ("w4a16_gemm.hip", "w4a16_decode.hip", "w4a16_wide.hip", "w4a16
                   "w4a16_epilogue.h",
                   "w4a16_layout.h", "w4a16_internal.h", "w4a16_api.cpp")
 KERNEL_SOURCES_W4A8 = ("w4a8_gemm.hip", "w4a8_device.h", "w4a8_internal.h", "w4a8_api.cpp")
+KERNEL_SOURCES_MXFP4 = ("mx_gemm.hip", "mx_internal.h", "mx_api.cpp")
 # Reported beside the headline workload (same protocol, no CPU baseline or
 # comparators): the prefill and the batched shapes of the same layer.
 EXTRA_WORKLOADS = ("prefill_m4096_k8192_n28672_bf16_asym_g128",
@@ -311,6 +313,41 @@ def run_workload(name, steps, warmup, rotate_bytes=1 << 30, with_cpu=True, compa
     return out
 
 
+def time_steps(step, steps, warmup):
+    """(ms per step over `steps` calls in one HIP graph between two events,
+    per-launch durations in ms from event pairs around each call)."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(steps):
+            step(i)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    graph.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / steps
+    del graph
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    hold_gpu(5.0 + 0.1 * steps)
+    for i in range(steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    return ms_step, np.array([a.elapsed_time(b) for a, b in ev])
+
+
 def w8_bytes(cfg):
     """Algorithmic bytes of one W4A8 call: the blob (codes, group constants,
     column scales), the int8 activations and their row scales, the fp16 output."""
@@ -340,38 +377,11 @@ def run_workload_w8(name, steps, warmup, rotate_bytes=1 << 30):
     copies = max(2, min(16, math.ceil(rotate_bytes / base.data.numel())))
     blobs = [base] + [w8.PackedW8(base.data.clone(), K, N, G) for _ in range(copies - 1)]
     Y = torch.empty((M, N), dtype=torch.float16, device=dev)
-    stream = torch.cuda.current_stream()
 
     def step(i):
         w8.w4a8_gemm(xq, sx, blobs[i % copies], out="fp16", Y=Y)
 
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for i in range(steps):
-            step(i)
-    torch.cuda.synchronize()
-    graph.replay()
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    graph.replay()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms_step = t0.elapsed_time(t1) / steps
-    del graph
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
-    hold_gpu(5.0 + 0.1 * steps)
-    for i in range(steps):
-        ev[i][0].record(stream)
-        step(i)
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    per_launch = np.array([a.elapsed_time(b) for a, b in ev])
+    ms_step, per_launch = time_steps(step, steps, warmup)
     nbytes = w8_bytes(cfg)
     ops = 2 * M * N * K
     gbs = nbytes / (ms_step * 1e-3) / 1e9
@@ -393,6 +403,60 @@ def run_workload_w8(name, steps, warmup, rotate_bytes=1 << 30):
         "config": {"workload": name, "M": M, "K": K, "N": N, "group_size": G,
                    "act": "int8 per row", "out": "fp16", "cold_weight_copies": copies,
                    "launch": "hip_graph_replay"},
+    }
+
+
+def mx_bytes(cfg):
+    """Algorithmic bytes of one MXFP4 call: the blob (E2M1 codes and E8M0
+    block scales), the E4M3 activations and their block scales, the fp16 output."""
+    M, K, N = cfg["M"], cfg["K"], cfg["N"]
+    return K * N // 2 + K * N // 32 + M * K + M * K // 32 + M * N * 2
+
+
+def run_workload_mx(name, steps, warmup, rotate_bytes=1 << 30):
+    """One MXFP4 workload (mxfp4_gemm, fp16 output), protocol of run_workload_w8."""
+    import torch
+
+    import w4a16_dequant_gemm_amd as w4
+    from w4a16_dequant_gemm_amd import mxfp4 as mx
+
+    w4.load_library()
+    cfg = dict(synth.MXFP4_WORKLOADS[name])
+    M, K, N = cfg["M"], cfg["K"], cfg["N"]
+    dev = torch.device("cuda:0")
+    p = synth.make_mxfp4_problem(seed=0, **cfg)
+    xq = torch.from_numpy(p.xq).to(dev)
+    xs = torch.from_numpy(p.xs).to(dev)
+    base = mx.mxfp4_repack(torch.from_numpy(p.qweight.view(np.int32)).to(dev),
+                           torch.from_numpy(p.ws).to(dev), K, N)
+    copies = max(2, min(16, math.ceil(rotate_bytes / base.data.numel())))
+    blobs = [base] + [mx.PackedMX(base.data.clone(), K, N) for _ in range(copies - 1)]
+    Y = torch.empty((M, N), dtype=torch.float16, device=dev)
+
+    def step(i):
+        mx.mxfp4_gemm(xq, xs, blobs[i % copies], out="fp16", Y=Y)
+
+    ms_step, per_launch = time_steps(step, steps, warmup)
+    nbytes = mx_bytes(cfg)
+    flops = 2 * M * N * K
+    gbs = nbytes / (ms_step * 1e-3) / 1e9
+    tf = flops / (ms_step * 1e-3) / 1e12
+    if flops / nbytes > FP8_PEAK_TFLOPS / HBM_PEAK_GBS * 1e3:
+        roof = {"bound": "mfma", "achieved": round(tf, 1), "peak": FP8_PEAK_TFLOPS,
+                "unit": "TFLOP/s (fp8 x fp4)", "frac": round(tf / FP8_PEAK_TFLOPS, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    roof["traffic"] = measured_traffic(name, KERNEL_SOURCES_MXFP4)
+    return {
+        "ms_per_step": round(ms_step, 5), "steps": steps, "kernel_us": round(ms_step * 1e3, 3),
+        "kernel_us_event_pairs_mean_p50": [round(float(np.mean(per_launch)) * 1e3, 3),
+                                           round(float(np.median(per_launch)) * 1e3, 3)],
+        "gbs": round(gbs, 1), "tflops": round(tf, 1), "algorithmic_bytes": nbytes,
+        "roofline": roof, "kernel_source_hash": kernel_source_hash(KERNEL_SOURCES_MXFP4),
+        "config": {"workload": name, "M": M, "K": K, "N": N, "block": 32,
+                   "act": "E4M3 + E8M0 per 32", "weight": "E2M1 + E8M0 per 32", "out": "fp16",
+                   "cold_weight_copies": copies, "launch": "hip_graph_replay"},
     }
 
 
@@ -538,7 +602,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
-                    help="a name from w4a16_synth.WORKLOADS or W4A8_WORKLOADS, 'all' (one "
+                    help="a name from w4a16_synth.WORKLOADS, W4A8_WORKLOADS or MXFP4_WORKLOADS, "
+                         "'all' (one "
                          "line each), or "
                          "one of " + ", ".join(LAYER_WORKLOADS) + " (fused FFN block)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -576,13 +641,15 @@ def main():
         name_, _, param = args.plan.partition(":")
         plan = (name_, int(param or 0))
     names = list(synth.WORKLOADS) if args.workload == "all" else args.workload.split(",")
-    if all(n in synth.W4A8_WORKLOADS for n in names):
+    if all(n in synth.W4A8_WORKLOADS or n in synth.MXFP4_WORKLOADS for n in names):
         for name in names:
-            out = run_workload_w8(name, args.steps, args.warmup)
-            out.update({"metric": "W4A8 GEMM achieved " + out["roofline"]["unit"],
+            w8 = name in synth.W4A8_WORKLOADS
+            out = (run_workload_w8 if w8 else run_workload_mx)(name, args.steps, args.warmup)
+            out.update({"metric": ("W4A8" if w8 else "MXFP4") + " GEMM achieved " +
+                        out["roofline"]["unit"],
                         "value": out["roofline"]["achieved"], "unit": out["roofline"]["unit"],
                         "n_gpus": 1, "warmup": args.warmup, "higher_is_better": True,
-                        "scaling": "weak", "vs_baseline": None, "dtype": "i8",
+                        "scaling": "weak", "vs_baseline": None, "dtype": "i8" if w8 else "fp8xfp4",
                         "data": "synthetic"})
             print(json.dumps(out), flush=True)
         return
@@ -593,6 +660,7 @@ def main():
         if len(names) == 1 and not args.no_extra and plan is None and args.m is None:
             out["extra_workloads"] = extra_workloads(name, min(args.steps, 50), min(args.warmup, 5))
             out["w4a8_workloads"] = w4a8_workloads(min(args.steps, 50), min(args.warmup, 5))
+            out["mxfp4_workloads"] = mxfp4_workloads(min(args.steps, 50), min(args.warmup, 5))
         print(json.dumps(out), flush=True)
 
 
@@ -624,6 +692,19 @@ def w4a8_workloads(steps, warmup):
         o = run_workload_w8(name, steps, warmup)
         res[name] = {k: o[k] for k in ("kernel_us", "ms_per_step", "steps", "roofline", "gbs",
                                        "tops_int8", "algorithmic_bytes")}
+        torch.cuda.empty_cache()
+    return res
+
+
+def mxfp4_workloads(steps, warmup):
+    """The MXFP4 route on its workloads, same protocol, same process."""
+    import torch
+
+    res = {}
+    for name in synth.MXFP4_WORKLOADS:
+        o = run_workload_mx(name, steps, warmup)
+        res[name] = {k: o[k] for k in ("kernel_us", "ms_per_step", "steps", "roofline", "gbs",
+                                       "tflops", "algorithmic_bytes")}
         torch.cuda.empty_cache()
     return res
 

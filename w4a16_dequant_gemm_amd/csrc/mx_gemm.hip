@@ -11,6 +11,9 @@
 // Compiled once per output dtype (MXFP4_TU_BF16 = 0 fp16, 1 bf16).
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+#include <utility>
+
 #include "mx_internal.h"
 
 #ifndef MXFP4_TU_BF16
@@ -56,17 +59,40 @@ __device__ __forceinline__ i32x8 widen(u32x4 w) {
     return r;
 }
 
+// A: E4M3 (format 0), B: E2M1 (format 4); the scales are byte SA of sa and
+// byte SB of sb (the instruction's byte select).
+template <int SA, int SB>
 __device__ __forceinline__ f32x16 mma(i32x8 a, i32x8 b, f32x16 c, int sa, int sb) {
-    // A: E4M3 (format 0), B: E2M1 (format 4); scale bytes in bits 0..7
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 4, 0, sa, 0, sb);
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 4, SA, sa, SB, sb);
 }
+
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>), in order:
+// a loop whose index is a compile-time constant in the body.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Scale words of one quad (4 k-steps) for a lane: B -- the dword whose byte u
+// is the tile's scale for k-step u; A -- per row tile the two dwords of the
+// row's 8 block scales, shifted right by 8*(lane/32) so that byte 2*(u%2) of
+// word u/2 is the lane's block 2u + lane/32.
+template <int RT, int CT>
+struct QuadScales {
+    uint32_t b[CT];
+    uint32_t a[RT][2];
+};
 
 // ---------------------------------------------------------------------------
 // Streaming kernel (M <= 64).  Wave w of a workgroup works on tile
-// blockIdx.x * (8/KP) + w / KP over part w % KP of the k-steps; per k-step a
-// lane needs 16 bytes of codes, the tile's scale byte, 2 x 16 bytes of X per
-// row tile and its row's scale byte, all in a ring of P k-steps in flight.
-// The KP parts of a tile add up in LDS in part order.
+// blockIdx.x * (8/KP) + w / KP over part w % KP of the k-steps (whole quads);
+// per k-step a lane needs 16 bytes of codes and 2 x 16 bytes of X per row
+// tile, in a ring of P k-steps in flight, and the quad's scale words, loaded
+// a quad ahead.  The KP parts of a tile add up in LDS in part order.
 // ---------------------------------------------------------------------------
 constexpr int kStreamDepth = 4;
 
@@ -84,7 +110,7 @@ __global__ __launch_bounds__(kMxWaves * 64) void mx_stream_kernel(
     const int KS = K / kStepK;
     const int KQ = K / kKAlign;
     const int t = blockIdx.x * CTW + ctl;
-    const int per = (KS + KP - 1) / KP;
+    const int per = ((KS + KP - 1) / KP + 3) & ~3;   // k-steps per part, whole quads
     const int c0 = min(part * per, KS);
     const int c1 = min(c0 + per, KS);
     const int n = c1 - c0;
@@ -93,12 +119,12 @@ __global__ __launch_bounds__(kMxWaves * 64) void mx_stream_kernel(
     const u32x4* wsrc = (const u32x4*)blob + (size_t)t * KS * 64 + lane;
     const uint8_t* ssrc = blob + s_off + (size_t)t * KQ * 256 + lane * 4;
     const uint8_t* xsrc[RT];
-    const uint8_t* xssrc[RT];
+    const uint8_t* xssrc[RT];   // the row's block scales, 8 per quad
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
         const int row = min(32 * r + (lane & 31), M - 1);
         xsrc[r] = X + (size_t)row * K + 16 * h;
-        xssrc[r] = XS + (size_t)row * (K / 32) + h;
+        xssrc[r] = XS + (size_t)row * (K / 32);
     }
 
     f32x16 acc[RT];
@@ -107,42 +133,60 @@ __global__ __launch_bounds__(kMxWaves * 64) void mx_stream_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[r][i] = 0.0f;
 
+    // codes and X in a ring of P = 4 k-steps; scales one quad ahead (the
+    // parts start on quad boundaries, so k-step c of the ring is byte c % 4)
+    static_assert(P == 4, "one quad of scales per ring turn");
     u32x4 wb[P];
-    uint32_t sbw[P];
     i32x4 xb[P][RT][2];
-    uint32_t sab[P][RT];
     auto fill = [&](int i, int c) __attribute__((always_inline)) {
         wb[i] = __builtin_nontemporal_load(wsrc + (size_t)c * 64);
-        sbw[i] = ssrc[(size_t)(c >> 2) * 256 + (c & 3)];
 #pragma unroll
         for (int r = 0; r < RT; ++r) {
             xb[i][r][0] = *(const i32x4*)(xsrc[r] + (size_t)c * kStepK);
             xb[i][r][1] = *(const i32x4*)(xsrc[r] + (size_t)c * kStepK + 32);
-            sab[i][r] = xssrc[r][2 * c];
         }
     };
+    QuadScales<RT, 1> cur, nxt;
+    auto load_quad = [&](QuadScales<RT, 1>& qs, int quad) __attribute__((always_inline)) {
+        qs.b[0] = *(const uint32_t*)(ssrc + (size_t)quad * 256);
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            const uint2 v = *(const uint2*)(xssrc[r] + (size_t)quad * 8);
+            qs.a[r][0] = v.x;
+            qs.a[r][1] = v.y;
+        }
+    };
+    auto shift_a = [&](QuadScales<RT, 1>& qs) __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            qs.a[r][0] >>= 8 * h;
+            qs.a[r][1] >>= 8 * h;
+        }
+    };
+    load_quad(cur, min(c0, c1 - 1) >> 2);
 #pragma unroll
     for (int i = 0; i < P; ++i) fill(i, min(c0 + i, c1 - 1));
+    shift_a(cur);
 
     for (int base = 0; base < n; base += P) {
-#pragma unroll
-        for (int i = 0; i < P; ++i) {
+        load_quad(nxt, min(c0 + base + P, c1 - 1) >> 2);
+        static_for<P>([&](auto ic) __attribute__((always_inline)) {
+            constexpr int i = decltype(ic)::value;
             const int c = c0 + base + i;
             if (base + i < n) {
                 const i32x8 b = widen(wb[i]);
-                const int sb = (int)sbw[i];
                 i32x8 a[RT];
-                int sa[RT];
 #pragma unroll
-                for (int r = 0; r < RT; ++r) {
-                    a[r] = cat(xb[i][r][0], xb[i][r][1]);
-                    sa[r] = (int)sab[i][r];
-                }
+                for (int r = 0; r < RT; ++r) a[r] = cat(xb[i][r][0], xb[i][r][1]);
                 fill(i, min(c + P, c1 - 1));
 #pragma unroll
-                for (int r = 0; r < RT; ++r) acc[r] = mma(a[r], b, acc[r], sa[r], sb);
+                for (int r = 0; r < RT; ++r)
+                    acc[r] = mma<2 * (i & 1), i>(a[r], b, acc[r], (int)cur.a[r][i >> 1],
+                                                 (int)cur.b[0]);
             }
-        }
+        });
+        shift_a(nxt);
+        cur = nxt;
     }
 
     if constexpr (KP > 1) {
@@ -178,9 +222,11 @@ __global__ __launch_bounds__(kMxWaves * 64) void mx_stream_kernel(
 // Tiled kernel (M > 32).  A workgroup owns BM = WM*RT*32 rows and BN =
 // WN*CT*32 columns over all of K.  X goes through a two-slot LDS ring (rows of
 // 64 bytes per k-step padded to 80, loaded two k-steps ahead), each wave's
-// codes and scale bytes through a register ring PD k-steps deep; the scale
-// bytes of X rows come straight from memory with the codes.  One barrier per
-// k-step; the XCD-grouped tile order of the W4A8 tiled kernel.
+// codes through a register ring of PD = 4 k-steps; the scale words of a quad
+// of k-steps (B: one dword per tile, A: 8 bytes per row tile) are loaded a
+// quad ahead and each k-step picks its byte with the instruction's byte
+// select.  One barrier per k-step; the XCD-grouped tile order of the W4A8
+// tiled kernel.
 // ---------------------------------------------------------------------------
 template <int RT, int CT, int WM, int WN, int PD, bool BF16>
 __global__ __launch_bounds__(kMxWaves * 64) void mx_tiled_kernel(
@@ -230,10 +276,10 @@ __global__ __launch_bounds__(kMxWaves * 64) void mx_tiled_kernel(
         wsrc[j] = (const u32x4*)blob + (size_t)tile[j] * KS * 64 + lane;
         ssrc[j] = blob + s_off + (size_t)tile[j] * KQ * 256 + lane * 4;
     }
-    const uint8_t* xssrc[RT];
+    const uint8_t* xssrc[RT];   // each row's block scales, 8 per quad
 #pragma unroll
     for (int r = 0; r < RT; ++r)
-        xssrc[r] = XS + (size_t)min(m0 + wm * RT * 32 + 32 * r + (lane & 31), M - 1) * (K / 32) + h;
+        xssrc[r] = XS + (size_t)min(m0 + wm * RT * 32 + 32 * r + (lane & 31), M - 1) * (K / 32);
 
     const uint8_t* xg[PIECES];
     int xl[PIECES];
@@ -254,18 +300,31 @@ __global__ __launch_bounds__(kMxWaves * 64) void mx_tiled_kernel(
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[r][j][i] = 0.0f;
 
-    // ring slot s: codes, B scale bytes and X scale bytes of the k-step c with c % PD == s
+    // ring slot s: the codes of the k-step c with c % PD == s; scales one
+    // quad ahead (PD == 4: ring slot s is byte s of the quad's scale words)
+    static_assert(PD == 4, "one quad of scales per ring turn");
     u32x4 wb[PD][CT];
-    uint32_t sbw[PD][CT];
-    uint32_t sab[PD][RT];
     auto fill = [&](int s, int c) __attribute__((always_inline)) {
 #pragma unroll
-        for (int j = 0; j < CT; ++j) {
-            wb[s][j] = __builtin_nontemporal_load(wsrc[j] + (size_t)c * 64);
-            sbw[s][j] = ssrc[j][(size_t)(c >> 2) * 256 + (c & 3)];
-        }
+        for (int j = 0; j < CT; ++j) wb[s][j] = __builtin_nontemporal_load(wsrc[j] + (size_t)c * 64);
+    };
+    QuadScales<RT, CT> cur, nxt;
+    auto load_quad = [&](QuadScales<RT, CT>& qs, int quad) __attribute__((always_inline)) {
 #pragma unroll
-        for (int r = 0; r < RT; ++r) sab[s][r] = xssrc[r][2 * c];
+        for (int j = 0; j < CT; ++j) qs.b[j] = *(const uint32_t*)(ssrc[j] + (size_t)quad * 256);
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            const uint2 v = *(const uint2*)(xssrc[r] + (size_t)quad * 8);
+            qs.a[r][0] = v.x;
+            qs.a[r][1] = v.y;
+        }
+    };
+    auto shift_a = [&](QuadScales<RT, CT>& qs) __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            qs.a[r][0] >>= 8 * h;
+            qs.a[r][1] >>= 8 * h;
+        }
     };
 
     // X two k-steps ahead: xr[c % 2] receives k-step c + 2 while c + 1 waits in the other
@@ -275,15 +334,18 @@ __global__ __launch_bounds__(kMxWaves * 64) void mx_tiled_kernel(
         xr[0][i] = *(const i32x4*)xg[i];
         xr[1][i] = *(const i32x4*)(xg[i] + (size_t)min(1, KS - 1) * kStepK);
     }
+    load_quad(cur, 0);
 #pragma unroll
     for (int s = 0; s < PD; ++s) fill(s, min(s, KS - 1));
 #pragma unroll
     for (int i = 0; i < PIECES; ++i) *(i32x4*)(lds + xl[i]) = xr[0][i];
+    shift_a(cur);
     __syncthreads();
 
     for (int cb = 0; cb < KS; cb += PD) {   // KS is a multiple of PD
-#pragma unroll
-        for (int q = 0; q < PD; ++q) {
+        load_quad(nxt, min(cb + PD, KS - 1) >> 2);
+        static_for<PD>([&](auto qc) __attribute__((always_inline)) {
+            constexpr int q = decltype(qc)::value;
             const int c = cb + q;
             const uint8_t* slot = lds + (q & 1) * SLOT;   // k-step c lives in LDS slot c % 2
             i32x4 (&xin)[PIECES] = xr[q & 1];
@@ -291,22 +353,17 @@ __global__ __launch_bounds__(kMxWaves * 64) void mx_tiled_kernel(
 #pragma unroll
             for (int i = 0; i < PIECES; ++i) xin[i] = *(const i32x4*)(xg[i] + (size_t)cn * kStepK);
             i32x8 b[CT];
-            int sb[CT];
 #pragma unroll
-            for (int j = 0; j < CT; ++j) {
-                b[j] = widen(wb[q][j]);
-                sb[j] = (int)sbw[q][j];
-            }
-            int sa[RT];
-#pragma unroll
-            for (int r = 0; r < RT; ++r) sa[r] = (int)sab[q][r];
+            for (int j = 0; j < CT; ++j) b[j] = widen(wb[q][j]);
             fill(q, min(c + PD, KS - 1));
 #pragma unroll
             for (int r = 0; r < RT; ++r) {
                 const i32x8 a = cat(*(const i32x4*)(slot + arow + r * 32 * RB),
                                     *(const i32x4*)(slot + arow + r * 32 * RB + 32));
 #pragma unroll
-                for (int j = 0; j < CT; ++j) acc[r][j] = mma(a, b[j], acc[r][j], sa[r], sb[j]);
+                for (int j = 0; j < CT; ++j)
+                    acc[r][j] = mma<2 * (q & 1), q>(a, b[j], acc[r][j], (int)cur.a[r][q >> 1],
+                                                    (int)cur.b[j]);
             }
             // LDS slot (c+1) % 2 was last read in k-step c-1, before the previous barrier
             uint8_t* next = lds + (1 - (q & 1)) * SLOT;
@@ -314,7 +371,9 @@ __global__ __launch_bounds__(kMxWaves * 64) void mx_tiled_kernel(
 #pragma unroll
             for (int i = 0; i < PIECES; ++i) *(i32x4*)(next + xl[i]) = xout[i];
             __syncthreads();
-        }
+        });
+        shift_a(nxt);
+        cur = nxt;
     }
 
 #pragma unroll
@@ -358,7 +417,7 @@ hipError_t launch_part(const uint8_t* xq, const uint8_t* xs, const void* packed,
         return launch_stream_kp<2>(xq, xs, packed, Y, M, L, plan, stream);
     }
     if (plan.cfg == 0)
-        mx_tiled_kernel<4, 2, 2, 4, 2, BF><<<plan.grid, kMxWaves * 64, plan.lds, stream>>>(
+        mx_tiled_kernel<4, 2, 2, 4, 4, BF><<<plan.grid, kMxWaves * 64, plan.lds, stream>>>(
             xq, xs, b, Y, (int)M, (int)L.N, (int)L.K, L.s_off, plan.nbm, plan.nbn);
     else if (plan.cfg == 1)
         mx_tiled_kernel<2, 1, 2, 4, 4, BF><<<plan.grid, kMxWaves * 64, plan.lds, stream>>>(
