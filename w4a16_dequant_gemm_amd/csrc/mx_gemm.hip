@@ -285,8 +285,11 @@ __global__ __launch_bounds__(kMxWaves * 64) void mx_tiled_kernel(
     int xl[PIECES];
 #pragma unroll
     for (int i = 0; i < PIECES; ++i) {
+        // 16 consecutive pieces: quarters 0..3 of rows b, b+4, b+8, b+12 (an
+        // 80-byte row stride puts those at dword offsets 0, 16, 32, 48 mod 64,
+        // so the 16-byte LDS writes of 16 lanes meet all 64 banks once)
         const int p = tid + kMxWaves * 64 * i;
-        const int row = p >> 2;
+        const int row = ((p >> 6) << 4) + (((p >> 2) & 3) << 2) + ((p >> 4) & 3);
         xg[i] = X + (size_t)min(m0 + row, M - 1) * K + 16 * (p & 3);
         xl[i] = row * RB + 16 * (p & 3);
     }

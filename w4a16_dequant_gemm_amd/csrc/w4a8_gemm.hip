@@ -234,13 +234,16 @@ __global__ __launch_bounds__(kW8Waves * 64) void w8_tiled_kernel(
         msrc[j] = (const uint16_t*)(blob + m_off) + (size_t)tile[j] * NG * 32 + (lane & 31);
     }
 
-    // X staging: piece p = tid + 512*i is row p/4, 16-byte quarter p%4.
+    // X staging: piece p = tid + 512*i is 16-byte quarter p%4 of a row.
     const int8_t* xg[PIECES];
     int xl[PIECES];
 #pragma unroll
     for (int i = 0; i < PIECES; ++i) {
+        // 16 consecutive pieces: quarters 0..3 of rows b, b+4, b+8, b+12 (an
+        // 80-byte row stride puts those at dword offsets 0, 16, 32, 48 mod 64,
+        // so the 16-byte LDS writes of 16 lanes meet all 64 banks once)
         const int p = tid + kW8Waves * 64 * i;
-        const int row = p >> 2;
+        const int row = ((p >> 6) << 4) + (((p >> 2) & 3) << 2) + ((p >> 4) & 3);
         xg[i] = X + (size_t)min(m0 + row, M - 1) * K + 16 * (p & 3);
         xl[i] = row * RB + 16 * (p & 3);
     }
