@@ -292,7 +292,7 @@ __global__ __launch_bounds__(SK_WAVES * 64) void splitk_kernel(
         }
     };
 
-    auto to_slot = [&]() {
+    auto to_slot = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int q = 0; q < QMAX; ++q) {
             if (q >= QM) break;
@@ -304,7 +304,7 @@ __global__ __launch_bounds__(SK_WAVES * 64) void splitk_kernel(
     };
 
     // Accumulators of a whole column block straight to Y.
-    auto to_y = [&](int nb) {
+    auto to_y = [&](int nb) __attribute__((always_inline)) {
         const int64_t col0 = (int64_t)nb * kColBlock + (lane & 31);
         uint16_t* ybase = Y + (size_t)(4 * (lane >> 5)) * N + col0;
 #pragma unroll
@@ -330,7 +330,7 @@ __global__ __launch_bounds__(SK_WAVES * 64) void splitk_kernel(
     // (LDS accesses through the __shared__ array itself: a generic pointer
     // would turn them into flat accesses, which count as vector memory
     // operations and would make the loop wait for every load in flight.)
-    auto balance = [&](int done_batches) {
+    auto balance = [&](int done_batches) __attribute__((always_inline)) {
         __hip_atomic_store(&s_prog[wave], done_batches, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_WORKGROUP);
         const int partner = __builtin_amdgcn_readfirstlane(__hip_atomic_load(
