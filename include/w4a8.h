@@ -58,7 +58,8 @@ extern "C" {
 /* Plan hints (w4a8_gemm flags only; for tests and benchmarks).  A hint that
  * does not apply to the shape is ignored.  W4A16_PLAN_PARAM(n) sets the
  * streaming kernel's parts of K per tile (2, 4 or 8), or the tiled kernel's
- * workgroup tile (1: 256 x 256, 2: 128 x 128, 3: 256 x 128). */
+ * workgroup tile (1: 256 x 256, 2: 128 x 128, 3: 256 x 128, 4: 256 x 256 with
+ * two chunks of K per LDS stage). */
 #define W4A8_PLAN_STREAM 0x10u   /* streaming kernel, M <= 64 */
 #define W4A8_PLAN_TILED  0x20u   /* LDS-tiled kernel */
 #define W4A8_PLAN_MASK   0x30u
@@ -120,7 +121,7 @@ w4a16_status_t w4a8_quantize_rows(const void *X, int8_t *xq, float *sx, int64_t 
  *   Y       dev, [M][N] of the output kind in flags.
  * Kernel choice (by M): the streaming kernel for M <= 32, the LDS-tiled
  * kernel above (workgroup tile 128 x 128 up to M = 128, 256 x 128 up to 512,
- * 256 x 256 beyond).
+ * 256 x 256 with two chunks of K per LDS stage beyond).
  * No workspace.  Calls on one stream may run back to back; Y must not
  * overlap the inputs.
  * Errors: INVALID_ARG, UNSUPPORTED, HIP.

@@ -355,6 +355,173 @@ __global__ __launch_bounds__(kW8Waves * 64) void w8_tiled_kernel(
     }
 }
 
+// The tiled kernel with two chunks (128 of K) per LDS stage: half the
+// barriers, each covering 2 x RT x CT x 2 MFMAs per wave.  Rows of 128 bytes
+// of X padded to 144; the 16-byte writes of 16 lanes go to rows b and b+8
+// (144-byte stride: 32 dwords apart), so they meet every bank once; the
+// operand reads of 16 consecutive rows do too (36-dword stride).  X one stage
+// ahead through registers, codes and group constants PD chunks ahead.
+template <int RT, int CT, int WM, int WN, int PD, bool G32, int OUT>
+__global__ __launch_bounds__(kW8Waves * 64) void w8_tiled2_kernel(
+    const int8_t* __restrict__ X, const float* __restrict__ sx, const uint8_t* __restrict__ blob,
+    void* __restrict__ Y, int M, int N, int K, int gshift, size_t m_off, size_t c_off, int nbm,
+    int nbn) {
+    static_assert(WM * WN == kW8Waves, "eight waves");
+    static_assert(4 % PD == 0, "the ring divides two stages");
+    constexpr int CK = 2;                               // chunks per LDS stage
+    constexpr int BM = WM * RT * 32;
+    constexpr int BN = WN * CT * 32;
+    constexpr int RB = 64 * CK + 16;
+    constexpr int SLOT = BM * RB;
+    constexpr int PIECES = BM * 4 * CK / (kW8Waves * 64);
+    static_assert(PIECES >= 1 && BM * 4 * CK == PIECES * kW8Waves * 64, "X staging");
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave / WN;
+    const int wn = wave % WN;
+    const int KC = K / kChunkK;
+    const int NT = N / kTileCols;
+    const int NG = G32 ? K / 32 : KC >> gshift;
+
+    const int T = nbm * nbn;
+    int task = blockIdx.x;
+    if (T % 8 == 0) task = (blockIdx.x % 8) * (T / 8) + blockIdx.x / 8;
+    constexpr int GM = 4;
+    const int group = task / (GM * nbn);
+    const int first_m = group * GM;
+    const int gsz = min(nbm - first_m, GM);
+    const int in_group = task % (GM * nbn);
+    const int mb = first_m + in_group % gsz;
+    const int nb = in_group / gsz;
+    const int m0 = mb * BM;
+
+    int tile[CT];
+    bool tile_ok[CT];
+    const u32x4* wsrc[CT];
+    const uint16_t* msrc[CT];
+#pragma unroll
+    for (int j = 0; j < CT; ++j) {
+        const int tt = nb * (BN / 32) + wn * CT + j;
+        tile_ok[j] = tt < NT;
+        tile[j] = min(tt, NT - 1);
+        wsrc[j] = (const u32x4*)blob + (size_t)tile[j] * KC * 64 + lane;
+        msrc[j] = (const uint16_t*)(blob + m_off) + (size_t)tile[j] * NG * 32 + (lane & 31);
+    }
+
+    // X staging: piece p covers 16-byte piece p%8 of a row: 16 consecutive
+    // pieces are rows b and b+8 of a group of 16 rows
+    const int8_t* xg[PIECES];
+    int xl[PIECES];
+#pragma unroll
+    for (int i = 0; i < PIECES; ++i) {
+        const int p = tid + kW8Waves * 64 * i;
+        const int q = p & 7;
+        const int row = ((p >> 7) << 4) + (((p >> 3) & 1) << 3) + ((p >> 4) & 7);
+        xg[i] = X + (size_t)min(m0 + row, M - 1) * K + 16 * q;
+        xl[i] = row * RB + 16 * q;
+    }
+    const int arow = (wm * RT * 32 + (lane & 31)) * RB + 16 * (lane >> 5);
+
+    i32x16 acc[RT][CT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int j = 0; j < CT; ++j)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[r][j][i] = 0;
+
+    u32x4 wb[PD][CT];
+    uint32_t mt[PD][CT][2];
+    auto fill = [&](int s, int c) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < CT; ++j) {
+            wb[s][j] = __builtin_nontemporal_load(wsrc[j] + (size_t)c * 64);
+            mt[s][j][0] = msrc[j][(size_t)group_of<G32>(c, 0, gshift) * 32];
+            mt[s][j][1] = G32 ? msrc[j][(size_t)group_of<G32>(c, 1, gshift) * 32] : 0u;
+        }
+    };
+    auto operands = [&](int s, i32x4 (&bq)[CT][2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < CT; ++j) {
+            const u32x4 w = wb[s][j];
+            bq[j][0] = operand_b(w[0], w[1], group_w8(mt[s][j][0]));
+            bq[j][1] = operand_b(w[2], w[3], group_w8(G32 ? mt[s][j][1] : mt[s][j][0]));
+        }
+    };
+
+    const int NS = KC / CK;   // stages (KC is a multiple of 4)
+    i32x4 xr[PIECES];
+#pragma unroll
+    for (int i = 0; i < PIECES; ++i) xr[i] = *(const i32x4*)xg[i];
+#pragma unroll
+    for (int s = 0; s < PD; ++s) fill(s, min(s, KC - 1));
+#pragma unroll
+    for (int i = 0; i < PIECES; ++i) *(i32x4*)(lds + xl[i]) = xr[i];
+    i32x4 bqa[CT][2], bqb[CT][2];
+    operands(0, bqa);
+    fill(0, min(PD, KC - 1));
+    __syncthreads();
+
+    for (int st0 = 0; st0 < NS; st0 += 2) {   // two stages per turn (NS is even)
+#pragma unroll
+        for (int sp = 0; sp < 2; ++sp) {
+            const int st = st0 + sp;
+            const uint8_t* slot = lds + sp * SLOT;   // stage st lives in LDS slot st % 2
+            const int sn = min(st + 1, NS - 1);
+#pragma unroll
+            for (int i = 0; i < PIECES; ++i)
+                xr[i] = *(const i32x4*)(xg[i] + (size_t)sn * (kChunkK * CK));
+#pragma unroll
+            for (int j2 = 0; j2 < CK; ++j2) {
+                const int q = sp * CK + j2;            // chunk index inside the turn (static)
+                const int c = st * CK + j2;
+                i32x4 (&cur)[CT][2] = (q & 1) ? bqb : bqa;
+                i32x4 (&nxt)[CT][2] = (q & 1) ? bqa : bqb;
+                const int sl = (q + 1) % PD;           // ring slot of chunk c+1
+                operands(sl, nxt);
+                fill(sl, min(c + 1 + PD, KC - 1));
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    i32x4 a[RT];
+#pragma unroll
+                    for (int r = 0; r < RT; ++r)
+                        a[r] = *(const i32x4*)(slot + arow + r * 32 * RB + j2 * kChunkK + 32 * s);
+#pragma unroll
+                    for (int r = 0; r < RT; ++r)
+#pragma unroll
+                        for (int j = 0; j < CT; ++j)
+                            acc[r][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[r], cur[j][s],
+                                                                              acc[r][j], 0, 0, 0);
+                }
+            }
+            // LDS slot (st+1) % 2 was last read in stage st-1, before the previous barrier
+            uint8_t* next = lds + (1 - sp) * SLOT;
+#pragma unroll
+            for (int i = 0; i < PIECES; ++i) *(i32x4*)(next + xl[i]) = xr[i];
+            __syncthreads();
+        }
+    }
+
+    const float* colscale = (const float*)(blob + c_off);
+#pragma unroll
+    for (int j = 0; j < CT; ++j) {
+        if (!tile_ok[j]) continue;
+        const int col = tile[j] * kTileCols + (lane & 31);
+        const float swn = OUT == OUT_I32 ? 0.0f : colscale[col];
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int row = m0 + wm * RT * 32 + 32 * r + acc_row_w8(i, lane);
+                if (row < M) store_out<OUT>(Y, (int64_t)row * N + col, acc[r][j][i],
+                                            OUT == OUT_I32 ? 0.0f : sx[row], swn);
+            }
+    }
+}
+
 template <int RT, int KP, bool G32>
 hipError_t launch_stream_t(const int8_t* xq, const float* sx, const void* packed, void* Y,
                            int64_t M, const LayoutW8& L, const PlanW8& plan, int gshift,
@@ -391,6 +558,11 @@ hipError_t launch_g(const int8_t* xq, const float* sx, const void* packed, void*
                                                              plan.nbm, plan.nbn);
     else if (plan.cfg == 1)
         w8_tiled_kernel<2, 1, 2, 4, 4, 2, G32, W4A8_TU_OUT>
+            <<<plan.grid, kW8Waves * 64, plan.lds, stream>>>(xq, sx, b, Y, (int)M, (int)L.N,
+                                                             (int)L.K, gshift, L.m_off, L.c_off,
+                                                             plan.nbm, plan.nbn);
+    else if (plan.cfg == 3)
+        w8_tiled2_kernel<4, 2, 2, 4, 2, G32, W4A8_TU_OUT>
             <<<plan.grid, kW8Waves * 64, plan.lds, stream>>>(xq, sx, b, Y, (int)M, (int)L.N,
                                                              (int)L.K, gshift, L.m_off, L.c_off,
                                                              plan.nbm, plan.nbn);
