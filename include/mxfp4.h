@@ -43,7 +43,7 @@ extern "C" {
 /* Plan hints (mxfp4_gemm flags only; tests and benchmarks).  A hint that does
  * not apply is ignored.  W4A16_PLAN_PARAM(n): the streaming kernel's parts of
  * K per tile (2, 4 or 8), or the tiled kernel's workgroup tile (1: 256 x 256,
- * 2: 128 x 128, 3: 256 x 128). */
+ * 2: 128 x 128, 3: 256 x 128, 4: 256 x 256 with two k-steps per LDS stage). */
 #define MXFP4_PLAN_STREAM 0x10u   /* streaming kernel, M <= 64 */
 #define MXFP4_PLAN_TILED  0x20u   /* LDS-tiled kernel */
 #define MXFP4_PLAN_MASK   0x30u

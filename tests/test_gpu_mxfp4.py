@@ -128,6 +128,7 @@ GEMM_CASES = [  # (M, K, N, plan)
     (3, 512, 384, "tiled"), (33, 512, 384, None), (64, 1024, 256, None), (100, 1024, 256, None),
     (130, 768, 640, None), (200, 512, 384, ("tiled", 3)), (300, 512, 128, None),
     (40, 1024, 640, ("tiled", 1)), (513, 1024, 384, None), (1000, 512, 640, None),
+    (300, 768, 640, ("tiled", 4)), (33, 1024, 128, ("tiled", 4)), (600, 512, 384, ("tiled", 1)),
 ]
 
 

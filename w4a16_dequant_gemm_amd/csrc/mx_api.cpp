@@ -48,17 +48,17 @@ PlanMX make_plan_mx(int64_t M, int64_t N, int64_t K, uint32_t flags) {
         p.lds = (size_t)(p.kp - 1) * ctw * p.rt * 16 * 64 * 4;
     } else {
         p.variant = MX_TILED;
-        p.cfg = (hint == MXFP4_PLAN_TILED && param >= 1 && param <= 3) ? param - 1
+        p.cfg = (hint == MXFP4_PLAN_TILED && param >= 1 && param <= 4) ? param - 1
                 : M <= 128                                              ? 1
                 : M <= 512                                              ? 2
-                                                                        : 0;
+                                                                        : 3;
         const int64_t bm = p.cfg == 1 ? 128 : 256;
-        const int64_t bn = p.cfg == 0 ? 256 : 128;
+        const int64_t bn = (p.cfg == 0 || p.cfg == 3) ? 256 : 128;
         p.rt = p.cfg == 1 ? 2 : 4;
         p.nbm = (int)((M + bm - 1) / bm);
         p.nbn = (int)((N + bn - 1) / bn);
         p.grid = p.nbm * p.nbn;
-        p.lds = (size_t)2 * bm * kMxRowBytes;
+        p.lds = (size_t)2 * bm * (p.cfg == 3 ? 2 * kStepK + 16 : kMxRowBytes);
     }
     return p;
 }

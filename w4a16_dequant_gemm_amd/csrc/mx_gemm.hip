@@ -220,15 +220,16 @@ __global__ __launch_bounds__(kMxWaves * 64) void mx_stream_kernel(
 
 // ---------------------------------------------------------------------------
 // Tiled kernel (M > 32).  A workgroup owns BM = WM*RT*32 rows and BN =
-// WN*CT*32 columns over all of K.  X goes through a two-slot LDS ring (rows of
-// 64 bytes per k-step padded to 80, loaded two k-steps ahead), each wave's
+// WN*CT*32 columns over all of K.  X goes through a two-slot LDS ring of CK
+// k-steps per slot (rows of 64*CK bytes padded by 16; CK = 1: loaded two
+// k-steps ahead; CK = 2: one stage ahead, half the barriers), each wave's
 // codes through a register ring of PD = 4 k-steps; the scale words of a quad
 // of k-steps (B: one dword per tile, A: 8 bytes per row tile) are loaded a
 // quad ahead and each k-step picks its byte with the instruction's byte
 // select.  One barrier per k-step; the XCD-grouped tile order of the W4A8
 // tiled kernel.
 // ---------------------------------------------------------------------------
-template <int RT, int CT, int WM, int WN, int PD, bool BF16>
+template <int RT, int CT, int WM, int WN, int PD, int CK, bool BF16>
 __global__ __launch_bounds__(kMxWaves * 64) void mx_tiled_kernel(
     const uint8_t* __restrict__ X, const uint8_t* __restrict__ XS, const uint8_t* __restrict__ blob,
     void* __restrict__ Y, int M, int N, int K, size_t s_off, int nbm, int nbn) {
@@ -236,10 +237,11 @@ __global__ __launch_bounds__(kMxWaves * 64) void mx_tiled_kernel(
     static_assert(PD % 2 == 0 && kKAlign / kStepK % PD == 0, "the ring divides the k-steps");
     constexpr int BM = WM * RT * 32;
     constexpr int BN = WN * CT * 32;
-    constexpr int RB = kMxRowBytes;
+    static_assert(CK == 1 || CK == 2, "one or two k-steps per LDS stage");
+    constexpr int RB = kStepK * CK + 16;
     constexpr int SLOT = BM * RB;
-    constexpr int PIECES = BM * 4 / (kMxWaves * 64);
-    static_assert(PIECES >= 1 && BM * 4 == PIECES * kMxWaves * 64, "X staging");
+    constexpr int PIECES = BM * 4 * CK / (kMxWaves * 64);
+    static_assert(PIECES >= 1 && BM * 4 * CK == PIECES * kMxWaves * 64, "X staging");
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
     const int tid = threadIdx.x;
@@ -289,9 +291,13 @@ __global__ __launch_bounds__(kMxWaves * 64) void mx_tiled_kernel(
         // 80-byte row stride puts those at dword offsets 0, 16, 32, 48 mod 64,
         // so the 16-byte LDS writes of 16 lanes meet all 64 banks once)
         const int p = tid + kMxWaves * 64 * i;
-        const int row = ((p >> 6) << 4) + (((p >> 2) & 3) << 2) + ((p >> 4) & 3);
-        xg[i] = X + (size_t)min(m0 + row, M - 1) * K + 16 * (p & 3);
-        xl[i] = row * RB + 16 * (p & 3);
+        // CK = 2: 16 consecutive pieces are the 8 pieces of rows b and b+8
+        // (144-byte stride: 32 dwords apart)
+        const int q = CK == 1 ? (p & 3) : (p & 7);
+        const int row = CK == 1 ? ((p >> 6) << 4) + (((p >> 2) & 3) << 2) + ((p >> 4) & 3)
+                                : ((p >> 7) << 4) + (((p >> 3) & 1) << 3) + ((p >> 4) & 7);
+        xg[i] = X + (size_t)min(m0 + row, M - 1) * K + 16 * q;
+        xl[i] = row * RB + 16 * q;
     }
     const int arow = (wm * RT * 32 + (lane & 31)) * RB + 16 * h;
 
@@ -330,12 +336,14 @@ __global__ __launch_bounds__(kMxWaves * 64) void mx_tiled_kernel(
         }
     };
 
-    // X two k-steps ahead: xr[c % 2] receives k-step c + 2 while c + 1 waits in the other
-    i32x4 xr[2][PIECES];
+    // X: CK = 1, two k-steps ahead (xr[c % 2] receives k-step c + 2 while c + 1
+    // waits in the other); CK = 2, one stage (two k-steps) ahead
+    constexpr int XR = CK == 1 ? 2 : 1;
+    i32x4 xr[XR][PIECES];
 #pragma unroll
     for (int i = 0; i < PIECES; ++i) {
         xr[0][i] = *(const i32x4*)xg[i];
-        xr[1][i] = *(const i32x4*)(xg[i] + (size_t)min(1, KS - 1) * kStepK);
+        if constexpr (CK == 1) xr[1][i] = *(const i32x4*)(xg[i] + (size_t)min(1, KS - 1) * kStepK);
     }
     load_quad(cur, 0);
 #pragma unroll
@@ -350,30 +358,38 @@ __global__ __launch_bounds__(kMxWaves * 64) void mx_tiled_kernel(
         static_for<PD>([&](auto qc) __attribute__((always_inline)) {
             constexpr int q = decltype(qc)::value;
             const int c = cb + q;
-            const uint8_t* slot = lds + (q & 1) * SLOT;   // k-step c lives in LDS slot c % 2
-            i32x4 (&xin)[PIECES] = xr[q & 1];
-            const int cn = min(c + 2, KS - 1);
+            constexpr int j2 = q % CK;                 // k-step inside its LDS stage
+            constexpr int sp = (q / CK) & 1;           // LDS slot of this stage
+            const uint8_t* slot = lds + sp * SLOT;
+            if constexpr (j2 == 0) {
+                // X of the stage CK k-steps ahead of this one (XR = 2: two ahead)
+                i32x4 (&xin)[PIECES] = xr[XR == 2 ? (q & 1) : 0];
+                const int cn = min(c + (CK == 1 ? 2 : CK), KS - CK);
 #pragma unroll
-            for (int i = 0; i < PIECES; ++i) xin[i] = *(const i32x4*)(xg[i] + (size_t)cn * kStepK);
+                for (int i = 0; i < PIECES; ++i)
+                    xin[i] = *(const i32x4*)(xg[i] + (size_t)cn * kStepK);
+            }
             i32x8 b[CT];
 #pragma unroll
             for (int j = 0; j < CT; ++j) b[j] = widen(wb[q][j]);
             fill(q, min(c + PD, KS - 1));
 #pragma unroll
             for (int r = 0; r < RT; ++r) {
-                const i32x8 a = cat(*(const i32x4*)(slot + arow + r * 32 * RB),
-                                    *(const i32x4*)(slot + arow + r * 32 * RB + 32));
+                const int off = arow + r * 32 * RB + j2 * kStepK;
+                const i32x8 a = cat(*(const i32x4*)(slot + off), *(const i32x4*)(slot + off + 32));
 #pragma unroll
                 for (int j = 0; j < CT; ++j)
                     acc[r][j] = mma<2 * (q & 1), q>(a, b[j], acc[r][j], (int)cur.a[r][q >> 1],
                                                     (int)cur.b[j]);
             }
-            // LDS slot (c+1) % 2 was last read in k-step c-1, before the previous barrier
-            uint8_t* next = lds + (1 - (q & 1)) * SLOT;
-            i32x4 (&xout)[PIECES] = xr[1 - (q & 1)];   // k-step c + 1
+            if constexpr (j2 == CK - 1) {
+                // the other LDS slot was last read in the stage before, before the previous barrier
+                uint8_t* next = lds + (1 - sp) * SLOT;
+                i32x4 (&xout)[PIECES] = xr[XR == 2 ? 1 - (q & 1) : 0];   // the next stage
 #pragma unroll
-            for (int i = 0; i < PIECES; ++i) *(i32x4*)(next + xl[i]) = xout[i];
-            __syncthreads();
+                for (int i = 0; i < PIECES; ++i) *(i32x4*)(next + xl[i]) = xout[i];
+                __syncthreads();
+            }
         });
         shift_a(nxt);
         cur = nxt;
@@ -420,13 +436,16 @@ hipError_t launch_part(const uint8_t* xq, const uint8_t* xs, const void* packed,
         return launch_stream_kp<2>(xq, xs, packed, Y, M, L, plan, stream);
     }
     if (plan.cfg == 0)
-        mx_tiled_kernel<4, 2, 2, 4, 4, BF><<<plan.grid, kMxWaves * 64, plan.lds, stream>>>(
+        mx_tiled_kernel<4, 2, 2, 4, 4, 1, BF><<<plan.grid, kMxWaves * 64, plan.lds, stream>>>(
             xq, xs, b, Y, (int)M, (int)L.N, (int)L.K, L.s_off, plan.nbm, plan.nbn);
     else if (plan.cfg == 1)
-        mx_tiled_kernel<2, 1, 2, 4, 4, BF><<<plan.grid, kMxWaves * 64, plan.lds, stream>>>(
+        mx_tiled_kernel<2, 1, 2, 4, 4, 1, BF><<<plan.grid, kMxWaves * 64, plan.lds, stream>>>(
+            xq, xs, b, Y, (int)M, (int)L.N, (int)L.K, L.s_off, plan.nbm, plan.nbn);
+    else if (plan.cfg == 3)
+        mx_tiled_kernel<4, 2, 2, 4, 4, 2, BF><<<plan.grid, kMxWaves * 64, plan.lds, stream>>>(
             xq, xs, b, Y, (int)M, (int)L.N, (int)L.K, L.s_off, plan.nbm, plan.nbn);
     else
-        mx_tiled_kernel<4, 1, 2, 4, 4, BF><<<plan.grid, kMxWaves * 64, plan.lds, stream>>>(
+        mx_tiled_kernel<4, 1, 2, 4, 4, 1, BF><<<plan.grid, kMxWaves * 64, plan.lds, stream>>>(
             xq, xs, b, Y, (int)M, (int)L.N, (int)L.K, L.s_off, plan.nbm, plan.nbn);
     return hipGetLastError();
 }

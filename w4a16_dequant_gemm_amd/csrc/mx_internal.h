@@ -69,7 +69,8 @@ struct PlanMX {
     VariantMX variant;
     int rt;          // 32-row tiles per wave
     int kp;          // STREAM: parts of K per tile
-    int cfg;         // TILED: workgroup tile 0 = 256 x 256, 1 = 128 x 128, 2 = 256 x 128
+    int cfg;         // TILED: workgroup tile 0 = 256 x 256, 1 = 128 x 128, 2 = 256 x 128,
+                     // 3 = 256 x 256 with two k-steps per LDS stage
     int grid;
     int nbm, nbn;
     size_t lds;
