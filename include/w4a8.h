@@ -59,7 +59,8 @@ extern "C" {
  * does not apply to the shape is ignored.  W4A16_PLAN_PARAM(n) sets the
  * streaming kernel's parts of K per tile (2, 4 or 8), or the tiled kernel's
  * workgroup tile (1: 256 x 256, 2: 128 x 128, 3: 256 x 128, 4: 256 x 256 with
- * two chunks of K per LDS stage). */
+ * two chunks of K per LDS stage, 5: the same with the int8 weights made once per
+ * workgroup in LDS). */
 #define W4A8_PLAN_STREAM 0x10u   /* streaming kernel, M <= 64 */
 #define W4A8_PLAN_TILED  0x20u   /* LDS-tiled kernel */
 #define W4A8_PLAN_MASK   0x30u

@@ -169,7 +169,8 @@ GEMM_CASES = [
     (40, 1024, 640, 64, ("tiled", 1)), (130, 512, 384, 128, ("tiled", 2)),
     (257, 768, 128, 64, ("tiled", 1)), (48, 512, 256, 64, ("stream", 2)),
     (600, 512, 384, 128, ("tiled", 4)), (300, 768, 640, 32, ("tiled", 4)),
-    (33, 1024, 128, 64, ("tiled", 4)),
+    (33, 1024, 128, 64, ("tiled", 4)), (300, 256, 384, 32, ("tiled", 5)),
+    (600, 512, 640, 128, ("tiled", 5)),
 ]
 
 

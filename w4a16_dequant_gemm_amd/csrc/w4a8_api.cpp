@@ -82,24 +82,27 @@ PlanW8 make_plan_w8(int64_t M, int64_t N, int64_t K, uint32_t flags, int cus) {
     } else {
         p.variant = W8_TILED;
         // tile shapes: 0 = 256 x 256 (4 x 2 tiles per wave), 1 = 128 x 128 (2 x 1),
-        // 2 = 256 x 128 (4 x 1), 3 = 256 x 256 with two chunks per LDS stage;
-        // W4A16_PLAN_PARAM(1 + shape) forces one
+        // 2 = 256 x 128 (4 x 1), 3 = 256 x 256 with two chunks per LDS stage,
+        // 4 = 3 with the int8 weights made once per workgroup in LDS (measured
+        // 4-7% slower than 3, not chosen by default); W4A16_PLAN_PARAM(1 + shape)
+        // forces one
         // (measured on the 8192 x 28672 layer: 128 x 128 is fastest up to M = 128,
         // 256 x 128 up to 512, 256 x 256 beyond)
         // (256 x 256 with two chunks per LDS stage: half the barriers, 3-11%
         // faster than one chunk per stage at M = 1024..4096)
-        p.cfg = (hint == W4A8_PLAN_TILED && param >= 1 && param <= 4) ? param - 1
+        p.cfg = (hint == W4A8_PLAN_TILED && param >= 1 && param <= 5) ? param - 1
                 : M <= 128                                            ? 1
                 : M <= 512                                            ? 2
                                                                       : 3;
         const int64_t bm = p.cfg == 1 ? 128 : 256;
-        const int64_t bn = (p.cfg == 0 || p.cfg == 3) ? 256 : 128;
+        const int64_t bn = (p.cfg == 0 || p.cfg == 3 || p.cfg == 4) ? 256 : 128;
         p.rt = p.cfg == 1 ? 2 : 4;
         p.nbm = (int)((M + bm - 1) / bm);
         p.nbn = (int)((N + bn - 1) / bn);
         p.grid = p.nbm * p.nbn;
         // two LDS slots of bm rows: 64 bytes of X per chunk (+16), or two chunks (cfg 3)
-        p.lds = (size_t)2 * bm * (p.cfg == 3 ? 2 * kChunkK + 16 : kTiledRowBytes);
+        p.lds = (size_t)2 * bm * (p.cfg >= 3 ? 2 * kChunkK + 16 : kTiledRowBytes);
+        if (p.cfg == 4) p.lds += (size_t)2 * (bn / kTileCols) * 2 * 2 * 1024;   // B operands
     }
     return p;
 }

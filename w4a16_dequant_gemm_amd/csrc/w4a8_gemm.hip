@@ -522,6 +522,175 @@ __global__ __launch_bounds__(kW8Waves * 64) void w8_tiled2_kernel(
     }
 }
 
+// The 256 x 256 tiled kernel with the int8 weights made once per workgroup
+// (page "W4A8量化计算优化", section 3.1: the weights of a tile are loaded and
+// prepared once for all the matrix work on them).  Per stage of two chunks
+// each of the 8 waves turns one column tile's codes into int8 B operands and
+// writes them to LDS in the operand order (lane l's 16 bytes of tile t, chunk
+// j, k-step s at ((t*2 + j)*2 + s)*1024 + 16*l), beside the stage's X rows;
+// after the barrier every wave reads the B operands of its CT tiles from LDS.
+// The dequant work per wave halves against the kernels above (there, the WM
+// waves sharing a column tile each make its operands), at the cost of 4 KiB
+// of LDS writes and 8 KiB of reads per wave and stage.  Stage s+1's operands
+// and X rows are made while stage s's MFMAs run; one barrier per stage.
+template <int RT, int CT, int WM, int WN, int PD, bool G32, int OUT>
+__global__ __launch_bounds__(kW8Waves * 64) void w8_coop_kernel(
+    const int8_t* __restrict__ X, const float* __restrict__ sx, const uint8_t* __restrict__ blob,
+    void* __restrict__ Y, int M, int N, int K, int gshift, size_t m_off, size_t c_off, int nbm,
+    int nbn) {
+    static_assert(WM * WN == kW8Waves && WN * CT == kW8Waves, "eight waves, eight column tiles");
+    static_assert(4 % PD == 0, "the ring divides two stages");
+    constexpr int CK = 2;                               // chunks per LDS stage
+    constexpr int NTB = WN * CT;                        // column tiles per workgroup (8)
+    constexpr int BM = WM * RT * 32;
+    constexpr int BN = NTB * 32;
+    constexpr int RB = 64 * CK + 16;
+    constexpr int XBYTES = BM * RB;
+    constexpr int BBYTES = NTB * CK * 2 * 1024;         // [tile][chunk][k-step][lane] 16 B
+    constexpr int SLOT = XBYTES + BBYTES;
+    constexpr int PIECES = BM * 4 * CK / (kW8Waves * 64);
+    static_assert(PIECES >= 1 && BM * 4 * CK == PIECES * kW8Waves * 64, "X staging");
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave / WN;
+    const int wn = wave % WN;
+    const int KC = K / kChunkK;
+    const int NT = N / kTileCols;
+    const int NG = G32 ? K / 32 : KC >> gshift;
+
+    const int T = nbm * nbn;
+    int task = blockIdx.x;
+    if (T % 8 == 0) task = (blockIdx.x % 8) * (T / 8) + blockIdx.x / 8;
+    constexpr int GM = 4;
+    const int group = task / (GM * nbn);
+    const int first_m = group * GM;
+    const int gsz = min(nbm - first_m, GM);
+    const int in_group = task % (GM * nbn);
+    const int mb = first_m + in_group % gsz;
+    const int nb = in_group / gsz;
+    const int m0 = mb * BM;
+
+    // the tile this wave prepares: workgroup tile `wave`
+    const int ptile = min(nb * NTB + wave, NT - 1);
+    const u32x4* wsrc = (const u32x4*)blob + (size_t)ptile * KC * 64 + lane;
+    const uint16_t* msrc = (const uint16_t*)(blob + m_off) + (size_t)ptile * NG * 32 + (lane & 31);
+    const int boff_w = wave * (CK * 2 * 1024) + lane * 16;   // its operands inside a slot's B area
+
+    const int8_t* xg[PIECES];
+    int xl[PIECES];
+#pragma unroll
+    for (int i = 0; i < PIECES; ++i) {
+        const int p = tid + kW8Waves * 64 * i;
+        const int q = p & 7;
+        const int row = ((p >> 7) << 4) + (((p >> 3) & 1) << 3) + ((p >> 4) & 7);
+        xg[i] = X + (size_t)min(m0 + row, M - 1) * K + 16 * q;
+        xl[i] = row * RB + 16 * q;
+    }
+    const int arow = (wm * RT * 32 + (lane & 31)) * RB + 16 * (lane >> 5);
+
+    i32x16 acc[RT][CT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int j = 0; j < CT; ++j)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[r][j][i] = 0;
+
+    // ring slot s: codes and group constants of this wave's tile for the chunk c with c % PD == s
+    u32x4 wb[PD];
+    uint32_t mt[PD][2];
+    auto fill = [&](int s, int c) __attribute__((always_inline)) {
+        wb[s] = __builtin_nontemporal_load(wsrc + (size_t)c * 64);
+        mt[s][0] = msrc[(size_t)group_of<G32>(c, 0, gshift) * 32];
+        mt[s][1] = G32 ? msrc[(size_t)group_of<G32>(c, 1, gshift) * 32] : 0u;
+    };
+    // the operands of chunk c (ring slot s) into chunk position j of an LDS slot's B area
+    auto produce = [&](uint8_t* bslot, int s, int j) __attribute__((always_inline)) {
+        const u32x4 w = wb[s];
+        const i32x4 b0 = operand_b(w[0], w[1], group_w8(mt[s][0]));
+        const i32x4 b1 = operand_b(w[2], w[3], group_w8(G32 ? mt[s][1] : mt[s][0]));
+        *(i32x4*)(bslot + boff_w + (j * 2 + 0) * 1024) = b0;
+        *(i32x4*)(bslot + boff_w + (j * 2 + 1) * 1024) = b1;
+    };
+
+    const int NS = KC / CK;   // stages (KC is a multiple of 4)
+    i32x4 xr[PIECES];
+#pragma unroll
+    for (int i = 0; i < PIECES; ++i) xr[i] = *(const i32x4*)xg[i];
+#pragma unroll
+    for (int s = 0; s < PD; ++s) fill(s, min(s, KC - 1));
+#pragma unroll
+    for (int i = 0; i < PIECES; ++i) *(i32x4*)(lds + xl[i]) = xr[i];
+    // stage 0's operands (chunks 0 and 1, ring slots 0 and 1), then their slots refilled
+#pragma unroll
+    for (int j = 0; j < CK; ++j) {
+        produce(lds + XBYTES, j % PD, j);
+        fill(j % PD, min(j + PD, KC - 1));
+    }
+    __syncthreads();
+
+    for (int st0 = 0; st0 < NS; st0 += 2) {   // two stages per turn (NS is even)
+#pragma unroll
+        for (int sp = 0; sp < 2; ++sp) {
+            const int st = st0 + sp;
+            const uint8_t* slot = lds + sp * SLOT;      // stage st lives in LDS slot st % 2
+            uint8_t* next = lds + (1 - sp) * SLOT;     // read in stage st-1, before the previous barrier
+            const int sn = min(st + 1, NS - 1);
+#pragma unroll
+            for (int i = 0; i < PIECES; ++i)
+                xr[i] = *(const i32x4*)(xg[i] + (size_t)sn * (kChunkK * CK));
+#pragma unroll
+            for (int j2 = 0; j2 < CK; ++j2) {
+                // this wave's share of stage st+1: chunk (st+1)*CK + j2, ring slot ((sp+1)*CK + j2) % PD
+                const int cq = ((sp + 1) * CK + j2) % PD;
+                produce(next + XBYTES, cq, j2);
+                fill(cq, min((st + 1) * CK + j2 + PD, KC - 1));
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    i32x4 a[RT];
+                    i32x4 bq[CT];
+#pragma unroll
+                    for (int r = 0; r < RT; ++r)
+                        a[r] = *(const i32x4*)(slot + arow + r * 32 * RB + j2 * kChunkK + 32 * s);
+#pragma unroll
+                    for (int j = 0; j < CT; ++j)
+                        bq[j] = *(const i32x4*)(slot + XBYTES + (wn * CT + j) * (CK * 2 * 1024) +
+                                               (j2 * 2 + s) * 1024 + lane * 16);
+#pragma unroll
+                    for (int r = 0; r < RT; ++r)
+#pragma unroll
+                        for (int j = 0; j < CT; ++j)
+                            acc[r][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[r], bq[j],
+                                                                              acc[r][j], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < PIECES; ++i) *(i32x4*)(next + xl[i]) = xr[i];
+            __syncthreads();
+        }
+    }
+
+    const float* colscale = (const float*)(blob + c_off);
+#pragma unroll
+    for (int j = 0; j < CT; ++j) {
+        const int tt = nb * NTB + wn * CT + j;
+        if (tt >= NT) continue;
+        const int col = tt * kTileCols + (lane & 31);
+        const float swn = OUT == OUT_I32 ? 0.0f : colscale[col];
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int row = m0 + wm * RT * 32 + 32 * r + acc_row_w8(i, lane);
+                if (row < M) store_out<OUT>(Y, (int64_t)row * N + col, acc[r][j][i],
+                                            OUT == OUT_I32 ? 0.0f : sx[row], swn);
+            }
+    }
+}
+
 template <int RT, int KP, bool G32>
 hipError_t launch_stream_t(const int8_t* xq, const float* sx, const void* packed, void* Y,
                            int64_t M, const LayoutW8& L, const PlanW8& plan, int gshift,
@@ -558,6 +727,11 @@ hipError_t launch_g(const int8_t* xq, const float* sx, const void* packed, void*
                                                              plan.nbm, plan.nbn);
     else if (plan.cfg == 1)
         w8_tiled_kernel<2, 1, 2, 4, 4, 2, G32, W4A8_TU_OUT>
+            <<<plan.grid, kW8Waves * 64, plan.lds, stream>>>(xq, sx, b, Y, (int)M, (int)L.N,
+                                                             (int)L.K, gshift, L.m_off, L.c_off,
+                                                             plan.nbm, plan.nbn);
+    else if (plan.cfg == 4)
+        w8_coop_kernel<4, 2, 2, 4, 4, G32, W4A8_TU_OUT>
             <<<plan.grid, kW8Waves * 64, plan.lds, stream>>>(xq, sx, b, Y, (int)M, (int)L.N,
                                                              (int)L.K, gshift, L.m_off, L.c_off,
                                                              plan.nbm, plan.nbn);

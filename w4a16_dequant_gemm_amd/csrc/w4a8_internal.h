@@ -91,7 +91,8 @@ struct PlanW8 {
     int rt;          // 32-row tiles per wave
     int kp;          // STREAM: parts of K per tile
     int cfg;         // TILED: workgroup tile 0 = 256 x 256, 1 = 128 x 128, 2 = 256 x 128,
-                     // 3 = 256 x 256 with two chunks per LDS stage
+                     // 3 = 256 x 256 with two chunks per LDS stage, 4 = the same with
+                     // the int8 weights made once per workgroup in LDS
     int grid;        // workgroups
     int nbm, nbn;    // TILED: row and column blocks
     size_t lds;      // dynamic LDS bytes
