@@ -234,7 +234,9 @@ __global__ __launch_bounds__(kMxWaves * 64) void mx_tiled_kernel(
     const uint8_t* __restrict__ X, const uint8_t* __restrict__ XS, const uint8_t* __restrict__ blob,
     void* __restrict__ Y, int M, int N, int K, size_t s_off, int nbm, int nbn) {
     static_assert(WM * WN == kMxWaves, "eight waves");
-    static_assert(PD % 2 == 0 && kKAlign / kStepK % PD == 0, "the ring divides the k-steps");
+    // the ring must divide the k-step count: KS is a multiple of 4, and of 8
+    // where the launcher picks PD = 8
+    static_assert(PD == 4 || PD == 8, "ring depth");
     constexpr int BM = WM * RT * 32;
     constexpr int BN = WN * CT * 32;
     static_assert(CK == 1 || CK == 2, "one or two k-steps per LDS stage");
@@ -310,8 +312,8 @@ __global__ __launch_bounds__(kMxWaves * 64) void mx_tiled_kernel(
             for (int i = 0; i < 16; ++i) acc[r][j][i] = 0.0f;
 
     // ring slot s: the codes of the k-step c with c % PD == s; scales one
-    // quad ahead (PD == 4: ring slot s is byte s of the quad's scale words)
-    static_assert(PD == 4, "one quad of scales per ring turn");
+    // quad ahead (k-step c is byte c % 4 of its quad's scale words)
+
     u32x4 wb[PD][CT];
     auto fill = [&](int s, int c) __attribute__((always_inline)) {
 #pragma unroll
@@ -354,10 +356,10 @@ __global__ __launch_bounds__(kMxWaves * 64) void mx_tiled_kernel(
     __syncthreads();
 
     for (int cb = 0; cb < KS; cb += PD) {   // KS is a multiple of PD
-        load_quad(nxt, min(cb + PD, KS - 1) >> 2);
         static_for<PD>([&](auto qc) __attribute__((always_inline)) {
             constexpr int q = decltype(qc)::value;
             const int c = cb + q;
+            if constexpr (q % 4 == 0) load_quad(nxt, min(c + 4, KS - 1) >> 2);
             constexpr int j2 = q % CK;                 // k-step inside its LDS stage
             constexpr int sp = (q / CK) & 1;           // LDS slot of this stage
             const uint8_t* slot = lds + sp * SLOT;
@@ -379,8 +381,8 @@ __global__ __launch_bounds__(kMxWaves * 64) void mx_tiled_kernel(
                 const i32x8 a = cat(*(const i32x4*)(slot + off), *(const i32x4*)(slot + off + 32));
 #pragma unroll
                 for (int j = 0; j < CT; ++j)
-                    acc[r][j] = mma<2 * (q & 1), q>(a, b[j], acc[r][j], (int)cur.a[r][q >> 1],
-                                                    (int)cur.b[j]);
+                    acc[r][j] = mma<2 * (q & 1), q % 4>(a, b[j], acc[r][j],
+                                                        (int)cur.a[r][(q % 4) >> 1], (int)cur.b[j]);
             }
             if constexpr (j2 == CK - 1) {
                 // the other LDS slot was last read in the stage before, before the previous barrier
@@ -390,9 +392,11 @@ __global__ __launch_bounds__(kMxWaves * 64) void mx_tiled_kernel(
                 for (int i = 0; i < PIECES; ++i) *(i32x4*)(next + xl[i]) = xout[i];
                 __syncthreads();
             }
+            if constexpr (q % 4 == 3) {
+                shift_a(nxt);
+                cur = nxt;
+            }
         });
-        shift_a(nxt);
-        cur = nxt;
     }
 
 #pragma unroll
@@ -437,6 +441,9 @@ hipError_t launch_part(const uint8_t* xq, const uint8_t* xs, const void* packed,
     }
     if (plan.cfg == 0)
         mx_tiled_kernel<4, 2, 2, 4, 4, 1, BF><<<plan.grid, kMxWaves * 64, plan.lds, stream>>>(
+            xq, xs, b, Y, (int)M, (int)L.N, (int)L.K, L.s_off, plan.nbm, plan.nbn);
+    else if (plan.cfg == 1 && L.KS % 8 == 0)   // codes 8 k-steps ahead where the ring divides K
+        mx_tiled_kernel<2, 1, 2, 4, 8, 1, BF><<<plan.grid, kMxWaves * 64, plan.lds, stream>>>(
             xq, xs, b, Y, (int)M, (int)L.N, (int)L.K, L.s_off, plan.nbm, plan.nbn);
     else if (plan.cfg == 1)
         mx_tiled_kernel<2, 1, 2, 4, 4, 1, BF><<<plan.grid, kMxWaves * 64, plan.lds, stream>>>(

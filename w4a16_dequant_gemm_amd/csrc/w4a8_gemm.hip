@@ -187,7 +187,9 @@ __global__ __launch_bounds__(kW8Waves * 64) void w8_tiled_kernel(
     void* __restrict__ Y, int M, int N, int K, int gshift, size_t m_off, size_t c_off, int nbm,
     int nbn) {
     static_assert(WM * WN == kW8Waves, "eight waves");
-    static_assert(PD % 2 == 0 && kKAlign / kChunkK % PD == 0, "the ring divides the chunk count");
+    // the ring must divide the chunk count: KC is a multiple of 4, and of 8
+    // where the launcher picks PD = 8
+    static_assert(PD == 2 || PD == 4 || PD == 8, "ring depth");
     static_assert(XD == 1 || XD == 2, "X is loaded one or two chunks ahead");
     constexpr int BM = WM * RT * 32;
     constexpr int BN = WN * CT * 32;
@@ -722,6 +724,11 @@ hipError_t launch_g(const int8_t* xq, const float* sx, const void* packed, void*
     }
     if (plan.cfg == 0)
         w8_tiled_kernel<4, 2, 2, 4, 2, (G32 ? 1 : 2), G32, W4A8_TU_OUT>
+            <<<plan.grid, kW8Waves * 64, plan.lds, stream>>>(xq, sx, b, Y, (int)M, (int)L.N,
+                                                             (int)L.K, gshift, L.m_off, L.c_off,
+                                                             plan.nbm, plan.nbn);
+    else if (plan.cfg == 1 && L.KC % 8 == 0)   // codes 8 chunks ahead where the ring divides K
+        w8_tiled_kernel<2, 1, 2, 4, 8, 2, G32, W4A8_TU_OUT>
             <<<plan.grid, kW8Waves * 64, plan.lds, stream>>>(xq, sx, b, Y, (int)M, (int)L.N,
                                                              (int)L.K, gshift, L.m_off, L.c_off,
                                                              plan.nbm, plan.nbn);
