@@ -97,3 +97,31 @@ def test_plan_hint_names(w8):
     assert w8.plan_flags_w8(("stream", 4)) == 0x10 | (4 << 8)
     with pytest.raises(ValueError):
         w8.plan_flags_w8("wide")
+
+
+def test_bindings_reject_bad_tensors_before_any_launch(w8):
+    """The Python bindings check what the C side cannot see (device, dtype,
+    element count, contiguity); these CPU tensors fail those checks, so no
+    pointer ever reaches a kernel."""
+    import torch
+    from w4a16_dequant_gemm_amd import mxfp4 as mx
+    K, N, G = 256, 128, 64
+    qw = torch.zeros((K // 8, N), dtype=torch.int32)
+    s8 = torch.zeros((K // G, N), dtype=torch.uint8)
+    with pytest.raises(w4.W4A16Error):
+        w8.w4a8_repack(qw, s8, s8, torch.zeros(N), K, N, G)            # CPU tensors
+    with pytest.raises(w4.W4A16Error):
+        w8.w4a8_repack(qw[:4], s8, s8, torch.zeros(N), K, N, G)        # short qweight
+    with pytest.raises(w4.W4A16Error):
+        w8.w4a8_quantize_rows(torch.zeros((2, K), dtype=torch.float32))
+    with pytest.raises(w4.W4A16Error):
+        mx.mxfp4_repack(qw, torch.zeros((K // 32, N), dtype=torch.uint8), K, N)
+    with pytest.raises(w4.W4A16Error):
+        mx.mxfp4_quantize_rows(torch.zeros((2, K), dtype=torch.float16))
+    packed = w8.PackedW8(torch.zeros(10, dtype=torch.uint8), K, N, G)
+    with pytest.raises(w4.W4A16Error):
+        w8.w4a8_gemm(torch.zeros((2, K), dtype=torch.int8), None, packed, out="fp16")
+    pm = mx.PackedMX(torch.zeros(10, dtype=torch.uint8), K, N)
+    with pytest.raises(w4.W4A16Error):
+        mx.mxfp4_gemm(torch.zeros((2, K), dtype=torch.uint8), torch.zeros((2, K // 32),
+                      dtype=torch.uint8), pm)
