@@ -25,12 +25,22 @@
 //
 // Activations.  X (M rows of K) is copied into LDS once per workgroup, rows
 // padded by 16 bytes so that the rows a quarter-wave reads at one k sit in
-// different banks; the A operand of each k-step is one ds_read_b128 per lane
-// (lane l: row min(l % 32, M - 1), 8 halves at 8 * (l / 32)).  Rows >= M feed
-// only accumulator rows that are never stored.
+// different banks; the A operand of each k-step is one ds_read_b128 per lane.
 //
-// MFMA: v_mfma_f32_32x32x16_{f16,bf16}, one per (k-step, tile); B operand =
-// lane l's dequantized word (column l % 32 of the tile, 8 k at 8 * (l / 32)).
+// MFMA: v_mfma_f32_16x16x32_{f16,bf16}, one per (k-step of 16, tile), half
+// the matrix-core cycles of the 32x32x16 form whose B operand the weight
+// words are laid out for.  B operand = lane l's dequantized word as it is:
+// column c = l % 32 of the tile, k = 8 * (l / 32) .. +7 of the k-step.  In
+// the 16x16x32 instruction lane l feeds column l % 16 and reduction slot
+// o = l / 16, so slot o carries the columns of half h = o % 2 of the tile
+// (c = 16h + l % 16) at k-half o / 2.  The A operand is block diagonal: row
+// i of the 16 belongs to half h(i) = (i / 4) % 2 and holds X row
+// x(i) = i % 4 + 4 * (i / 8) in the slots of its own half and zeros in the
+// other two (and zeros if x(i) >= M), so that D row i, column j sums column
+// 16 h(i) + j of the tile only.  With that assignment lane l's accumulator
+// register r is column c = l % 32, X row 4 * (l / 32) + r: the lane's own
+// column, the same placement as registers 0..3 of the 32x32 form.  Zero
+// operands are read from a 512-byte zero strip in LDS.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -65,16 +75,15 @@ __global__ __launch_bounds__(DW * 64) void decode_kernel(
     constexpr int R = PB + 1;                // bodies held per wave (ring)
     constexpr int EARLY = kDecodeEarlyBodies < PB ? kDecodeEarlyBodies : PB;
     // Scale after the product (fp16, at most 8 rows): each group's MFMAs
-    // multiply X by the exact (q - z) into a temporary accumulator t, then
-    // the rows that can hold outputs (registers 0..3: rows 0..7) take
-    // acc += s * t, one fp32 fma per row instead of a v_pk_mul_f16 per
-    // weight pair.  t's registers 0..3 are zeroed at the start of each group
-    // (the other twelve only ever feed rows 8..31, which are never read; they
-    // start at zero and stay finite).  The sum differs from the dequantized-weight product
+    // multiply X by the exact (q - z) into a temporary accumulator t (zeroed
+    // at the start of each group), then acc += s * t, one fp32 fma per
+    // register instead of a v_pk_mul_f16 per weight pair (every register of
+    // a lane is its own column, whose scale it holds).  The sum differs from the dequantized-weight product
     // only by the rounding of each weight to fp16 (at most 2^-11 of each
     // term), and stays exact where the pages' result is: q = z gives products
     // of exact zeros, a one-hot row gives s * (q - z) rounded once.
     constexpr bool SA = kDecodeScaleAfter && DT == DT_F16 && MB == 8 && TPI == 1;
+    static_assert(MB == 8, "one 8-row group: the 16x16x32 tile holds 2 x 8 rows");
     extern __shared__ __align__(16) uint8_t lds[];
 
     const int tid = threadIdx.x;
@@ -112,12 +121,13 @@ __global__ __launch_bounds__(DW * 64) void decode_kernel(
     auto len_of = [&](int j) { return is_tail(j) ? ntb : nbw; };
 
     // LDS: X rows (row stride RS bytes), the partial-tile slots of two
-    // items, their two arrival counters, two counts of reduced items and the
-    // waves' progress counters
+    // items, their two arrival counters, two counts of reduced items, the
+    // waves' progress counters and the zero strip
     const int RS = 2 * K + 16;
     f32x4* slots = (f32x4*)(lds + (size_t)M * RS);   // [2][DW][TPI][QMAX][64]
     uint32_t* cnt = (uint32_t*)(slots + 2 * DW * TPI * QMAX * 64);
     uint32_t* prog = cnt + 4;                        // [DW] bodies computed per wave
+    u32x4* zstrip = (u32x4*)(prog + DW);             // kDecodeZeroBytes of zeros
     auto slot = [&](int par, int w, int tt, int q) -> f32x4& {
         return slots[(((par * DW + w) * TPI + tt) * QMAX + q) * 64 + lane];
     };
@@ -216,6 +226,7 @@ __global__ __launch_bounds__(DW * 64) void decode_kernel(
     // counters zeroed before any wave can reach an item end; no global load
     // has been issued yet, so this barrier costs only the waves' start skew
     if (tid < 4 + DW) cnt[tid] = 0u;
+    if (tid < kDecodeZeroBytes / 16) zstrip[tid] = u32x4{};
     __syncthreads();
     if (nbw == 0) return;                          // fewer bodies than waves: no work
     const int npl = (npc + 63) / 64;               // pieces per lane
@@ -234,23 +245,29 @@ __global__ __launch_bounds__(DW * 64) void decode_kernel(
     // consecutive MFMAs do not wait for each other's result: two for a single
     // tile, one each when several tiles interleave
     constexpr int NACC = TPI == 1 ? 2 : 1;
-    f32x16 acc[TPI][NACC];
+    f32x4 acc[TPI][NACC];
 #pragma unroll
     for (int tt = 0; tt < TPI; ++tt)
 #pragma unroll
-        for (int h = 0; h < NACC; ++h) acc[tt][h] = f32x16{};
-    f32x4 acc_sa = f32x4{};                      // scale-after: rows 0..7 of the tile
-    f32x16 t_sa = f32x16{};                      // scale-after: one group's product
+        for (int h = 0; h < NACC; ++h) acc[tt][h] = f32x4{};
+    f32x4 acc_sa = f32x4{};                      // scale-after: the tile
+    f32x4 t_sa = f32x4{};                        // scale-after: one group's product
 
     const Magic mg = make_magic();
     const uint32_t zsh = zent_shift<G>(c32);   // this lane's zero entry in its dword
-    // A operand address of this lane: row min(l % 32, M - 1), halves 8 * (l / 32)
-    const uint32_t arow = (uint32_t)min(c32, M - 1) * RS + 16 * (lane >> 5);
+    // A operand of this lane (row i = l % 16, slot o = l / 16): X row x(i) at
+    // halves 8 * (o / 2) of each k-step if row i's half is the slot's and
+    // x(i) < M, else the zero strip
+    const int ai = lane & 15;
+    const int axr = (ai & 3) + 4 * (ai >> 3);
+    const bool alive = ((ai >> 2) & 1) == ((lane >> 4) & 1) && axr < M;
+    const uint32_t arow = (uint32_t)axr * RS + 16 * (lane >> 5);
+    const uint32_t azero = (uint32_t)((const uint8_t*)zstrip - lds);
 
     // One body: the 16 A operands are read from LDS first (all in flight
     // together), then each k-step's words are dequantized and fed to the MFMAs.
     auto compute = [&](const Bundle& B, int b, auto ex) {
-        const uint8_t* abase = lds + arow + (size_t)b * (kBodyK * 2);
+        const uint8_t* abase = lds + (alive ? arow + (uint32_t)b * (kBodyK * 2) : azero);
         u32x4 a[16];
 #pragma unroll
         for (int kk = 0; kk < 16; ++kk) a[kk] = *(const u32x4*)(abase + kk * (kKStep * 2));
@@ -277,7 +294,7 @@ __global__ __launch_bounds__(DW * 64) void decode_kernel(
 #pragma unroll
                         for (int r = 0; r < 4; ++r) t_sa[r] = opaque_f(0.f);
                     }
-                    t_sa = mfma32x32x16<DT>(a[kk], bop, t_sa);
+                    t_sa = mfma16x16x32<DT>(a[kk], bop, t_sa);
                     if (kk % GS == GS - 1) {
 #pragma unroll
                         for (int r = 0; r < 4; ++r) acc_sa[r] = __builtin_fmaf(sc, t_sa[r], acc_sa[r]);
@@ -301,7 +318,7 @@ __global__ __launch_bounds__(DW * 64) void decode_kernel(
 #pragma unroll
                 for (int tt = 0; tt < TPI; ++tt) {
                     const u32x4 bop = dequant_sel<decltype(ex)::value>(B.w[tt][cc][u], prm[tt], mg);
-                    acc[tt][kk % NACC] = mfma32x32x16<DT>(a[kk], bop, acc[tt][kk % NACC]);
+                    acc[tt][kk % NACC] = mfma16x16x32<DT>(a[kk], bop, acc[tt][kk % NACC]);
                 }
             }
         }
@@ -394,18 +411,15 @@ __global__ __launch_bounds__(DW * 64) void decode_kernel(
 #pragma unroll
                 for (int q = 0; q < QMAX; ++q)
                     if (q < QM) {
-                        f32x4 v = f32x4{acc[tt][0][4 * q], acc[tt][0][4 * q + 1],
-                                        acc[tt][0][4 * q + 2], acc[tt][0][4 * q + 3]};
+                        f32x4 v = acc[tt][0];
 #pragma unroll
-                        for (int h = 1; h < NACC; ++h)
-                            v += f32x4{acc[tt][h][4 * q], acc[tt][h][4 * q + 1],
-                                       acc[tt][h][4 * q + 2], acc[tt][h][4 * q + 3]};
+                        for (int h = 1; h < NACC; ++h) v += acc[tt][h];
                         slot(par, wave, tt, q) = v;
                     }
 #pragma unroll
             for (int tt = 0; tt < TPI; ++tt)
 #pragma unroll
-                for (int h = 0; h < NACC; ++h) acc[tt][h] = f32x16{};
+                for (int h = 0; h < NACC; ++h) acc[tt][h] = f32x4{};
         }
         // the slot writes are complete (LDS only: loads in flight stay in flight)
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");

@@ -319,6 +319,26 @@ __device__ __forceinline__ f32x16 mfma32x32x16<DT_BF16>(u32x4 a, u32x4 b, f32x16
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// D = A.B + C on one 16x16x32 tile.  A: lane l holds row l%16, reduction
+// indices 8*(l/16)..+7; B: lane l holds column l%16, the same indices; C/D:
+// lane l, register r holds row 4*(l/16) + r, column l%16.  As for the 32x32
+// form, only the lane groups matter: lanes 16o..16o+15 of A and of B supply
+// the same eight reduction indices.
+template <int DT>
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c);
+
+template <>
+__device__ __forceinline__ f32x4 mfma16x16x32<DT_F16>(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+template <>
+__device__ __forceinline__ f32x4 mfma16x16x32<DT_BF16>(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
 // fp32 -> activation dtype, round to nearest even.
 template <int DT>
 __device__ __forceinline__ uint16_t round_out(float v);

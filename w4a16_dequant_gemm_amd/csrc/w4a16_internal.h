@@ -51,10 +51,12 @@ inline size_t wide_lds_bytes(int64_t M, int sk) { return (size_t)4 * M * (2 * sk
 
 // LDS bytes of a decode launch: M rows of X (2K bytes + 16 padding each), the
 // [2 items][waves][tiles per item][row groups][64 lanes] fp32x4 partial-tile
-// slots, four counters and one progress counter per wave.
+// slots, four counters, one progress counter per wave and the zero strip that
+// the empty blocks of the MFMA's A operand read (one body of k, 512 bytes).
+constexpr int kDecodeZeroBytes = 512;
 inline size_t decode_lds_bytes(int64_t M, int64_t K, int tpi, int mb) {
     return (size_t)M * (size_t)(2 * K + 16) + (size_t)2 * kDecodeWaves * tpi * (mb / 8) * 64 * 16 +
-           16 + 4 * kDecodeWaves;
+           16 + 4 * kDecodeWaves + kDecodeZeroBytes;
 }
 
 // How one w4a16_gemm call is executed.  Computed on the host from the shape
