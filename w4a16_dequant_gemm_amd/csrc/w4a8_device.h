@@ -60,6 +60,10 @@ __device__ __forceinline__ i32x4 operand_b(uint32_t w0, uint32_t w1, GroupW8 g) 
     return r;
 }
 
+// Buffer resource word 3 of a raw (unstrided) buffer with range checking:
+// a load at an offset past num_records returns zeros.
+constexpr int kRawBufferWord3 = 0x00020000;
+
 // Accumulator register r of lane l -> row offset inside a 32x32 tile.
 __device__ __forceinline__ int acc_row_w8(int r, int lane) {
     return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);

@@ -15,6 +15,8 @@
 // Compiled once per output kind (W4A8_TU_OUT = 0 fp16, 1 bf16, 2 int32).
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "w4a8_device.h"
 #include "w4a8_internal.h"
 
@@ -56,13 +58,30 @@ __device__ __forceinline__ int group_of(int c, int s, int gshift) {
 // X per row tile and k-step (X is small and stays in L2); all three ride in a
 // ring of P chunks in flight.  Then two k-steps of RT MFMAs.  The KP parts of
 // a tile add up in LDS.
+//
+// BD (M <= 8; the plan uses it up to M = 4): v_mfma_i32_16x16x64_i8 instead
+// of the 32x32x32 form, half the matrix-core cycles per k-step, on the same B
+// operands.  In the 16x16x64 instruction lane l feeds column l % 16 of
+// reduction slot o = l / 16; with
+// the B operand of the 32x32 layout (column l % 32, k-half l / 32) slot o
+// holds the columns of tile half o % 2 at k-half o / 2.  The A operand is
+// block diagonal: row i of the 16 belongs to half (i / 4) % 2, carries X row
+// i % 4 + 4 * (i / 8) in the slots of its own half and zeros elsewhere (and
+// for X rows >= M), so D row i sums only tile column 16 * ((i / 4) % 2) + j.
+// Lane l's four accumulator registers are then its own column l % 32, X rows
+// 4 * (l / 32) + r.  The zeros cost nothing: those lanes read X through a
+// buffer resource at an offset past its end, which returns zeros.
 // ---------------------------------------------------------------------------
 constexpr int kStreamDepth = 4;   // chunks in flight per wave
+constexpr uint32_t kPastEnd = 0x40000000u;   // > M * K of any stream launch
 
-template <int RT, int KP, bool G32, int OUT>
+template <int RT, int KP, bool G32, int OUT, bool BD>
 __global__ __launch_bounds__(kW8Waves * 64) void w8_stream_kernel(
     const int8_t* __restrict__ X, const float* __restrict__ sx, const uint8_t* __restrict__ blob,
     void* __restrict__ Y, int M, int N, int K, int gshift, size_t m_off, size_t c_off) {
+    static_assert(!BD || RT == 1, "the block-diagonal form holds 8 rows");
+    using Acc = typename std::conditional<BD, i32x4, i32x16>::type;
+    constexpr int NR = BD ? 4 : 16;   // accumulator registers per lane
     constexpr int CTW = kW8Waves / KP;
     constexpr int P = kStreamDepth;
     extern __shared__ int red[];
@@ -84,12 +103,22 @@ __global__ __launch_bounds__(kW8Waves * 64) void w8_stream_kernel(
 #pragma unroll
     for (int r = 0; r < RT; ++r)
         xsrc[r] = X + (size_t)min(32 * r + (lane & 31), M - 1) * K + 16 * (lane >> 5);
+    // BD: lane l is A row i = l % 16 of slot l / 16; its X row, or past the end
+    const __amdgpu_buffer_rsrc_t xrs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)X, (short)0, BD ? M * K : 0, kRawBufferWord3);
+    uint32_t xoff = 0;
+    if constexpr (BD) {
+        const int ai = lane & 15;
+        const int axr = (ai & 3) + 4 * (ai >> 3);
+        const bool alive = ((ai >> 2) & 1) == ((lane >> 4) & 1) && axr < M;
+        xoff = alive ? (uint32_t)(axr * K + 16 * (lane >> 5)) : kPastEnd;
+    }
 
-    i32x16 acc[RT];
+    Acc acc[RT];
 #pragma unroll
     for (int r = 0; r < RT; ++r)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[r][i] = 0;
+        for (int i = 0; i < NR; ++i) acc[r][i] = 0;
 
     // Ring of P chunks in flight: slot i holds chunk c0 + base + i -- its
     // codes, its group constants and its X operands.  Slot i is refilled with
@@ -99,10 +128,17 @@ __global__ __launch_bounds__(kW8Waves * 64) void w8_stream_kernel(
     uint32_t mb[P][2];
     auto fill = [&](int i, int c) __attribute__((always_inline)) {
         wb[i] = __builtin_nontemporal_load(wsrc + (size_t)c * 64);
+        if constexpr (BD) {
+            const uint32_t o = xoff + (uint32_t)c * kChunkK;
+            xb[i][0][0] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, o, 0, 0));
+            xb[i][0][1] =
+                __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, o + 32, 0, 0));
+        } else {
 #pragma unroll
-        for (int r = 0; r < RT; ++r) {
-            xb[i][r][0] = *(const i32x4*)(xsrc[r] + (size_t)c * kChunkK);
-            xb[i][r][1] = *(const i32x4*)(xsrc[r] + (size_t)c * kChunkK + 32);
+            for (int r = 0; r < RT; ++r) {
+                xb[i][r][0] = *(const i32x4*)(xsrc[r] + (size_t)c * kChunkK);
+                xb[i][r][1] = *(const i32x4*)(xsrc[r] + (size_t)c * kChunkK + 32);
+            }
         }
         mb[i][0] = msrc[(size_t)group_of<G32>(c, 0, gshift) * 32];
         mb[i][1] = G32 ? msrc[(size_t)group_of<G32>(c, 1, gshift) * 32] : 0u;
@@ -127,12 +163,17 @@ __global__ __launch_bounds__(kW8Waves * 64) void w8_stream_kernel(
                 fill(i, min(c + P, c1 - 1));
                 const i32x4 b0 = operand_b(w[0], w[1], group_w8(m0));
                 const i32x4 b1 = operand_b(w[2], w[3], group_w8(m1));
+                if constexpr (BD) {
+                    acc[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xa[0][0], b0, acc[0], 0, 0, 0);
+                    acc[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xa[0][1], b1, acc[0], 0, 0, 0);
+                } else {
 #pragma unroll
-                for (int r = 0; r < RT; ++r)
-                    acc[r] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xa[r][0], b0, acc[r], 0, 0, 0);
+                    for (int r = 0; r < RT; ++r)
+                        acc[r] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xa[r][0], b0, acc[r], 0, 0, 0);
 #pragma unroll
-                for (int r = 0; r < RT; ++r)
-                    acc[r] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xa[r][1], b1, acc[r], 0, 0, 0);
+                    for (int r = 0; r < RT; ++r)
+                        acc[r] = __builtin_amdgcn_mfma_i32_32x32x32_i8(xa[r][1], b1, acc[r], 0, 0, 0);
+                }
             }
         }
     }
@@ -143,8 +184,8 @@ __global__ __launch_bounds__(kW8Waves * 64) void w8_stream_kernel(
 #pragma unroll
             for (int r = 0; r < RT; ++r)
 #pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    red[((((part - 1) * CTW + ctl) * RT + r) * 16 + i) * 64 + lane] = acc[r][i];
+                for (int i = 0; i < NR; ++i)
+                    red[((((part - 1) * CTW + ctl) * RT + r) * NR + i) * 64 + lane] = acc[r][i];
         }
         __syncthreads();
         if (part > 0) return;
@@ -153,8 +194,8 @@ __global__ __launch_bounds__(kW8Waves * 64) void w8_stream_kernel(
 #pragma unroll
             for (int r = 0; r < RT; ++r)
 #pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    acc[r][i] += red[((((p - 1) * CTW + ctl) * RT + r) * 16 + i) * 64 + lane];
+                for (int i = 0; i < NR; ++i)
+                    acc[r][i] += red[((((p - 1) * CTW + ctl) * RT + r) * NR + i) * 64 + lane];
     }
 
     const int col = t * kTileCols + (lane & 31);
@@ -162,8 +203,8 @@ __global__ __launch_bounds__(kW8Waves * 64) void w8_stream_kernel(
 #pragma unroll
     for (int r = 0; r < RT; ++r)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int row = 32 * r + acc_row_w8(i, lane);
+        for (int i = 0; i < NR; ++i) {
+            const int row = BD ? 4 * (lane >> 5) + i : 32 * r + acc_row_w8(i, lane);
             if (row < M) store_out<OUT>(Y, (int64_t)row * N + col, acc[r][i],
                                         OUT == OUT_I32 ? 0.0f : sx[row], swn);
         }
@@ -697,7 +738,17 @@ template <int RT, int KP, bool G32>
 hipError_t launch_stream_t(const int8_t* xq, const float* sx, const void* packed, void* Y,
                            int64_t M, const LayoutW8& L, const PlanW8& plan, int gshift,
                            hipStream_t stream) {
-    w8_stream_kernel<RT, KP, G32, W4A8_TU_OUT><<<plan.grid, kW8Waves * 64, plan.lds, stream>>>(
+    if constexpr (RT == 1) {
+        if (plan.bd) {
+            if (M > 8) return hipErrorInvalidValue;   // the plan never asks for it
+            w8_stream_kernel<1, KP, G32, W4A8_TU_OUT, true>
+                <<<plan.grid, kW8Waves * 64, plan.lds, stream>>>(xq, sx, (const uint8_t*)packed, Y,
+                                                                 (int)M, (int)L.N, (int)L.K, gshift,
+                                                                 L.m_off, L.c_off);
+            return hipGetLastError();
+        }
+    }
+    w8_stream_kernel<RT, KP, G32, W4A8_TU_OUT, false><<<plan.grid, kW8Waves * 64, plan.lds, stream>>>(
         xq, sx, (const uint8_t*)packed, Y, (int)M, (int)L.N, (int)L.K, gshift, L.m_off, L.c_off);
     return hipGetLastError();
 }

@@ -90,6 +90,7 @@ struct PlanW8 {
     VariantW8 variant;
     int rt;          // 32-row tiles per wave
     int kp;          // STREAM: parts of K per tile
+    bool bd;         // STREAM, M <= 4: v_mfma_i32_16x16x64_i8 with a block-diagonal A
     int cfg;         // TILED: workgroup tile 0 = 256 x 256, 1 = 128 x 128, 2 = 256 x 128,
                      // 3 = 256 x 256 with two chunks per LDS stage, 4 = the same with
                      // the int8 weights made once per workgroup in LDS
