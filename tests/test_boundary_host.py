@@ -97,6 +97,13 @@ def test_plan_hints(lib):
     # area plus 2 x 128 partial tiles of 8 rows x 32 columns (fp32)
     assert w4.w4a16_workspace_bytes(4, 28672, 8192, 128, f) == 65536 + 2 * 128 * 1024
     assert w4.w4a16_workspace_bytes(4, 28672, 8192, 128, f | w4.plan_flags(("decode", 224))) == 0
+    # 128 tiles over 256 workgroups: whole tiles up to K = 8192 (no workspace),
+    # split in halves beyond, or when the workgroup count is forced
+    assert w4.w4a16_workspace_bytes(1, 4096, 4096, 128, f) == 0
+    assert w4.w4a16_workspace_bytes(4, 4096, 8192, 128, f) == 0
+    assert w4.w4a16_workspace_bytes(1, 4096, 16384, 128, f) == 65536 + 2 * 128 * 1024
+    assert w4.w4a16_workspace_bytes(1, 2048, 4096, 128, f) == 0
+    assert w4.w4a16_workspace_bytes(1, 2048, 4096, 128, f | w4.plan_flags(("decode", 255))) > 0
     # wide kernel: 224 blocks of 128 columns fill the workgroups, no workspace;
     # 64 blocks are split into 4 parts (4 tiles x 2 row tiles x 16 x 64 floats each)
     assert w4.w4a16_workspace_bytes(64, 28672, 8192, 128, f | w4.plan_flags("wide")) == 0

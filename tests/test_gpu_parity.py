@@ -241,7 +241,8 @@ def test_workspace_counters_return_to_zero():
                                         (40, 4096, 1024, "tiled"), (3, 8192, 1024, "splitk"),
                                         (70, 8192, 384, "tiled"), (2, 8192, 4096, "splitk"),
                                         (1, 4096, 256, "splitk"), (5, 8192, 8192, "splitk"),
-                                        (1, 4096, 1024, "decode"), (8, 8192, 4096, "decode"),
+                                        (1, 4096, 1024, ("decode", 255)),
+                                        (8, 8192, 2048, ("decode", 255)),
                                         (64, 4096, 512, "wide"), (100, 2048, 1024, "wide"),
                                         (4, 2048, 512, "splitk")]):
         p = synth.make_problem(M, K, N, G=128, seed=i)

@@ -120,10 +120,17 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int G, uint32_t flags) {
         p.items = (int)NT;
         p.waves = kDecodeWaves;
         int64_t W = cus;
-        if (hint == W4A16_PLAN_DECODE && param > 0) W = param;   // forced workgroup count
+        const bool forced = hint == W4A16_PLAN_DECODE && param > 0;
+        if (forced) W = param;   // forced workgroup count
         const int64_t F = NT / W, R = NT % W;
         int64_t S = R > 0 ? std::min<int64_t>({W / R, K / kBodyK / kDecodeWaves, 8}) : 1;
         if (S < 2 || R > kMaxTilesSplit) S = 1;
+        // Fewer tiles than workgroups (F = 0): every tile would be split, and
+        // every workgroup would end with a cross-workgroup meeting.  Measured
+        // on MI355X (us per call, graph replay): K = N = 4096 M = 1 6.2
+        // unsplit vs 7.35 in halves, M = 4 6.55 vs 7.8; K = 8192 N = 4096
+        // 7.9 vs 8.7.  So tiles stay whole there unless K is larger.
+        if (F == 0 && K <= kDecodeWholeTileMaxK && !forced) S = 1;
         p.grid_x = (int)(S > 1 ? (F > 0 ? W : R * S) : std::min<int64_t>(NT, W));
         p.grid_y = 1;
         p.grid_z = 1;

@@ -35,6 +35,9 @@ constexpr bool kDecodeBalance = true;
 // fp16, M <= 8: the group scale multiplies the MFMA's product of X and the
 // exact (q - z) instead of every weight.
 constexpr bool kDecodeScaleAfter = true;
+// With fewer tiles than workgroups, the decode kernel keeps tiles whole (no
+// split along K) up to this K.
+constexpr int64_t kDecodeWholeTileMaxK = 8192;
 // LDS budget of the decode kernel (X rows + partial-tile slots), per workgroup.
 constexpr size_t kDecodeLdsMax = 160 * 1024;
 
