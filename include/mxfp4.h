@@ -56,7 +56,8 @@ size_t mxfp4_packed_bytes(int64_t K, int64_t N);
  * Offline repack into the kernels' order (page "量化开销对比", section 6.4).
  *   qweight  dev, uint32 [K/8][N]; nibble i (bits 4i..4i+3) of word [r][n] is
  *            the E2M1 code of w[8r+i][n].
- *   ws       dev, uint8 [K/32][N], E8M0 block scales.
+ *   ws       dev, uint8 [K/32][N], E8M0 block scales; 0xFF (the E8M0 NaN) makes
+ *            its column of Y NaN, and the repack records its presence in the blob.
  *   packed   dev, output, packed_bytes >= mxfp4_packed_bytes(K, N).
  */
 w4a16_status_t mxfp4_repack(const uint32_t *qweight, const uint8_t *ws, int64_t K, int64_t N,
@@ -79,8 +80,9 @@ w4a16_status_t mxfp4_quantize_rows(const void *X, uint8_t *xq, uint8_t *xs, int6
  * Y = the product defined at the top of this file.
  *   xq  dev, uint8 [M][K] E4M3 codes; xs dev, uint8 [M][K/32] E8M0 scales;
  *   packed  a blob of mxfp4_repack for (K, N);  Y dev, fp16 or bf16 [M][N].
- * Kernel choice (by M): a streaming kernel for M <= 32, the LDS-tiled kernel
- * above.  No workspace.
+ * Kernel choice (by M): a streaming kernel for M <= 32 (on the 16x16x128 form
+ * of the instruction for M <= 4 unless the blob holds a NaN weight scale), the
+ * LDS-tiled kernel above.  No workspace.
  */
 w4a16_status_t mxfp4_gemm(const uint8_t *xq, const uint8_t *xs, const void *packed,
                           size_t packed_bytes, void *Y, int64_t M, int64_t N, int64_t K,

@@ -129,6 +129,9 @@ GEMM_CASES = [  # (M, K, N, plan)
     (130, 768, 640, None), (200, 512, 384, ("tiled", 3)), (300, 512, 128, None),
     (40, 1024, 640, ("tiled", 1)), (513, 1024, 384, None), (1000, 512, 640, None),
     (300, 768, 640, ("tiled", 4)), (33, 1024, 128, ("tiled", 4)), (600, 512, 384, ("tiled", 1)),
+    # the block-diagonal streaming form (M <= 8) with every parts count
+    (2, 512, 128, ("stream", 4)), (4, 1024, 256, ("stream", 2)), (8, 2048, 384, ("stream", 8)),
+    (5, 4096, 640, None), (6, 8192, 128, None),
 ]
 
 

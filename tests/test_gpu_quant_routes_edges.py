@@ -1,8 +1,8 @@
 """Edge cases and HIP-graph capture of the W4A8 and MXFP4 routes, through the
 C ABI: graph replays equal eager calls bit for bit (with eager work and
 synchronisations between replays), all-zero activations give exact zeros,
-one-hot activation rows reproduce the int8 weights exactly, and a NaN in one
-MX activation row stays in that row."""
+one-hot activation rows reproduce the int8 weights exactly, a NaN in one MX
+activation row stays in that row and a NaN MX weight scale in its column."""
 import numpy as np
 import pytest
 
@@ -115,19 +115,43 @@ def test_one_hot_rows_reproduce_int8_weights():
         assert np.array_equal(Y.astype(np.int64), w[ks])
 
 
-def test_mx_nan_activation_stays_in_its_row():
-    M, K, N = 12, 512, 256
+@pytest.mark.parametrize("M,row", [(12, 5), (3, 1), (1, 0)])
+def test_mx_nan_activation_stays_in_its_row(M, row):
+    K, N = 512, 256
     p = synth.make_mxfp4_problem(M, K, N, seed=7)
     mx, pk = _mx(p)
     xq = p.xq.copy()
-    xq[5, 100] = 0x7F                      # E4M3 NaN
-    say("mxfp4 NaN row")
+    xq[row, 100] = 0x7F                    # E4M3 NaN
+    say(f"mxfp4 NaN row M={M}")
     Y = mx.mxfp4_gemm(torch.from_numpy(xq).cuda(), torch.from_numpy(p.xs).cuda(), pk,
                       out="fp16").float().cpu().numpy()
     Y0 = mx.mxfp4_gemm(torch.from_numpy(p.xq).cuda(), torch.from_numpy(p.xs).cuda(), pk,
                        out="fp16").float().cpu().numpy()
-    assert np.all(np.isnan(Y[5]))
-    others = np.arange(M) != 5
+    assert np.all(np.isnan(Y[row]))
+    others = np.arange(M) != row
     assert np.array_equal(Y[others], Y0[others])
     _, y, B = omx.gemm(p.xq, p.xs, p.qweight, p.ws, M, N, K, "fp16")
     assert np.max(np.abs(Y0 - y) / np.where(B > 0, B, 1)) <= 2e-3
+
+
+@pytest.mark.parametrize("M", [1, 3, 12])
+def test_mx_nan_weight_scale_stays_in_its_column(M):
+    """An E8M0 NaN (0xFF) weight scale makes its own column NaN and no other:
+    the repack flags it, and the small-M kernel then keeps each column's
+    scales to itself."""
+    K, N = 512, 256
+    p = synth.make_mxfp4_problem(M, K, N, seed=8)
+    mx, pk0 = _mx(p)
+    ws = p.ws.copy()
+    ws[3, 37] = 0xFF                       # block 3 of column 37
+    pk = mx.mxfp4_repack(torch.from_numpy(p.qweight.view(np.int32)).to("cuda"),
+                         torch.from_numpy(ws).to("cuda"), K, N)
+    say(f"mxfp4 NaN weight scale M={M}")
+    xq = torch.from_numpy(p.xq).cuda()
+    xs = torch.from_numpy(p.xs).cuda()
+    Y = mx.mxfp4_gemm(xq, xs, pk, out="fp16").float().cpu().numpy()
+    Y0 = mx.mxfp4_gemm(xq, xs, pk0, out="fp16").float().cpu().numpy()
+    assert np.all(np.isnan(Y[:, 37]))
+    others = np.arange(N) != 37
+    assert not np.any(np.isnan(Y[:, others]))
+    assert np.array_equal(Y[:, others], Y0[:, others])

@@ -171,6 +171,9 @@ GEMM_CASES = [
     (600, 512, 384, 128, ("tiled", 4)), (300, 768, 640, 32, ("tiled", 4)),
     (33, 1024, 128, 64, ("tiled", 4)), (300, 256, 384, 32, ("tiled", 5)),
     (600, 512, 640, 128, ("tiled", 5)),
+    # the block-diagonal streaming form (M <= 4) with every parts count
+    (2, 1024, 256, 64, ("stream", 2)), (4, 2048, 384, 32, ("stream", 8)),
+    (3, 512, 128, 128, ("stream", 4)), (4, 8192, 128, 128, None),
 ]
 
 

@@ -26,6 +26,7 @@ namespace {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -66,6 +67,16 @@ __device__ __forceinline__ f32x16 mma(i32x8 a, i32x8 b, f32x16 c, int sa, int sb
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 4, SA, sa, SB, sb);
 }
 
+// The same on the 16x16x128 form.
+template <int SA, int SB>
+__device__ __forceinline__ f32x4 mma16(i32x8 a, i32x8 b, f32x4 c, int sa, int sb) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, SA, sa, SB, sb);
+}
+
+// Buffer resource word 3 of a raw (unstrided) buffer with range checking:
+// a load at an offset past num_records returns zeros.
+constexpr int kRawBufferWord3 = 0x00020000;
+
 // f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>), in order:
 // a loop whose index is a compile-time constant in the body.
 template <class F, int... I>
@@ -93,16 +104,41 @@ struct QuadScales {
 // per k-step a lane needs 16 bytes of codes and 2 x 16 bytes of X per row
 // tile, in a ring of P k-steps in flight, and the quad's scale words, loaded
 // a quad ahead.  The KP parts of a tile add up in LDS in part order.
+//
+// BD (M <= 8; the plan uses it up to M = 4): v_mfma_scale_f32_16x16x128_f8f6f4,
+// half the matrix-core cycles of the 32x32x64 form, on the same B operands and
+// B scales.  In the
+// 16x16x128 instruction B lane l holds column l % 16 at reduction indices
+// 32 * (l / 16) .. +31 (block l / 16), so block p carries the columns of tile
+// half p % 2 at k-half p / 2 of the k-step; A lane l holds row l % 16, bytes
+// 0..15 at 16 * (l / 16) + j and bytes 16..31 at 64 + 16 * (l / 16) + j (block
+// (l / 16) / 2 and 2 + (l / 16) / 2); each lane's scale byte is that of row
+// l % 16, block l / 16 (measured on gfx950).  The A operand is block
+// diagonal: row i of the 16 belongs to half (i / 4) % 2 and carries X row
+// x(i) = i % 4 + 4 * (i / 8); its lane in group o = l / 16 is live iff o / 2
+// is that half (then bytes 0..15 are X at k = 64s + 16 * (o % 2) + j and
+// bytes 16..31 at 64s + 32 + 16 * (o % 2) + j, the pattern of the 32x32 form
+// with l / 32 replaced by o % 2) and x(i) < M; other lanes read zeros past
+// the end of a buffer resource.  Lane l's A scale is row x(i)'s, block
+// 2s + l / 32, as in the 32x32 form.  Lane l's four accumulator registers
+// are its own column l % 32, X rows 4 * (l / 32) + r.  An empty A block
+// still meets the B scale of the other half's column, so a NaN (0xFF) weight
+// scale would reach a second column: blobs whose repack flagged one take
+// the 32x32 form.
 // ---------------------------------------------------------------------------
 constexpr int kStreamDepth = 4;
+constexpr uint32_t kPastEnd = 0x40000000u;   // >= M * K of any block-diagonal launch
 
-template <int RT, int KP, bool BF16>
-__global__ __launch_bounds__(kMxWaves * 64) void mx_stream_kernel(
-    const uint8_t* __restrict__ X, const uint8_t* __restrict__ XS, const uint8_t* __restrict__ blob,
-    void* __restrict__ Y, int M, int N, int K, size_t s_off) {
+template <int RT, int KP, bool BF16, bool BD>
+__device__ __forceinline__ void stream_body(const uint8_t* __restrict__ X,
+                                            const uint8_t* __restrict__ XS,
+                                            const uint8_t* __restrict__ blob, void* __restrict__ Y,
+                                            int M, int N, int K, size_t s_off, float* red) {
+    static_assert(!BD || RT == 1, "the block-diagonal form holds 8 rows");
+    using Acc = typename std::conditional<BD, f32x4, f32x16>::type;
+    constexpr int NR = BD ? 4 : 16;   // accumulator registers per lane
     constexpr int CTW = kMxWaves / KP;
     constexpr int P = kStreamDepth;
-    extern __shared__ float red[];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int part = wave % KP;
@@ -126,12 +162,22 @@ __global__ __launch_bounds__(kMxWaves * 64) void mx_stream_kernel(
         xsrc[r] = X + (size_t)row * K + 16 * h;
         xssrc[r] = XS + (size_t)row * (K / 32);
     }
+    const __amdgpu_buffer_rsrc_t xrs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)X, (short)0, BD ? M * K : 0, kRawBufferWord3);
+    uint32_t xoff = 0;
+    if constexpr (BD) {
+        const int ai = lane & 15;
+        const int axr = (ai & 3) + 4 * (ai >> 3);
+        const bool alive = (lane >> 5) == ((ai >> 2) & 1) && axr < M;
+        xoff = alive ? (uint32_t)axr * (uint32_t)K + 16u * (uint32_t)((lane >> 4) & 1) : kPastEnd;
+        xssrc[0] = XS + (size_t)min(axr, M - 1) * (K / 32);
+    }
 
-    f32x16 acc[RT];
+    Acc acc[RT];
 #pragma unroll
     for (int r = 0; r < RT; ++r)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[r][i] = 0.0f;
+        for (int i = 0; i < NR; ++i) acc[r][i] = 0.0f;
 
     // codes and X in a ring of P = 4 k-steps; scales one quad ahead (the
     // parts start on quad boundaries, so k-step c of the ring is byte c % 4)
@@ -140,10 +186,17 @@ __global__ __launch_bounds__(kMxWaves * 64) void mx_stream_kernel(
     i32x4 xb[P][RT][2];
     auto fill = [&](int i, int c) __attribute__((always_inline)) {
         wb[i] = __builtin_nontemporal_load(wsrc + (size_t)c * 64);
+        if constexpr (BD) {
+            const uint32_t o = xoff + (uint32_t)c * kStepK;
+            xb[i][0][0] = __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, o, 0, 0));
+            xb[i][0][1] =
+                __builtin_bit_cast(i32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, o + 32, 0, 0));
+        } else {
 #pragma unroll
-        for (int r = 0; r < RT; ++r) {
-            xb[i][r][0] = *(const i32x4*)(xsrc[r] + (size_t)c * kStepK);
-            xb[i][r][1] = *(const i32x4*)(xsrc[r] + (size_t)c * kStepK + 32);
+            for (int r = 0; r < RT; ++r) {
+                xb[i][r][0] = *(const i32x4*)(xsrc[r] + (size_t)c * kStepK);
+                xb[i][r][1] = *(const i32x4*)(xsrc[r] + (size_t)c * kStepK + 32);
+            }
         }
     };
     QuadScales<RT, 1> cur, nxt;
@@ -179,10 +232,15 @@ __global__ __launch_bounds__(kMxWaves * 64) void mx_stream_kernel(
 #pragma unroll
                 for (int r = 0; r < RT; ++r) a[r] = cat(xb[i][r][0], xb[i][r][1]);
                 fill(i, min(c + P, c1 - 1));
+                if constexpr (BD) {
+                    acc[0] = mma16<2 * (i & 1), i>(a[0], b, acc[0], (int)cur.a[0][i >> 1],
+                                                   (int)cur.b[0]);
+                } else {
 #pragma unroll
-                for (int r = 0; r < RT; ++r)
-                    acc[r] = mma<2 * (i & 1), i>(a[r], b, acc[r], (int)cur.a[r][i >> 1],
-                                                 (int)cur.b[0]);
+                    for (int r = 0; r < RT; ++r)
+                        acc[r] = mma<2 * (i & 1), i>(a[r], b, acc[r], (int)cur.a[r][i >> 1],
+                                                     (int)cur.b[0]);
+                }
             }
         });
         shift_a(nxt);
@@ -194,8 +252,8 @@ __global__ __launch_bounds__(kMxWaves * 64) void mx_stream_kernel(
 #pragma unroll
             for (int r = 0; r < RT; ++r)
 #pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    red[((((part - 1) * CTW + ctl) * RT + r) * 16 + i) * 64 + lane] = acc[r][i];
+                for (int i = 0; i < NR; ++i)
+                    red[((((part - 1) * CTW + ctl) * RT + r) * NR + i) * 64 + lane] = acc[r][i];
         }
         __syncthreads();
         if (part > 0) return;
@@ -204,18 +262,37 @@ __global__ __launch_bounds__(kMxWaves * 64) void mx_stream_kernel(
 #pragma unroll
             for (int r = 0; r < RT; ++r)
 #pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    acc[r][i] += red[((((p - 1) * CTW + ctl) * RT + r) * 16 + i) * 64 + lane];
+                for (int i = 0; i < NR; ++i)
+                    acc[r][i] += red[((((p - 1) * CTW + ctl) * RT + r) * NR + i) * 64 + lane];
     }
 
     const int col = t * kTileCols + (lane & 31);
 #pragma unroll
     for (int r = 0; r < RT; ++r)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int row = 32 * r + acc_row(i, lane);
+        for (int i = 0; i < NR; ++i) {
+            const int row = BD ? 4 * h + i : 32 * r + acc_row(i, lane);
             if (row < M) store_out<BF16>(Y, (int64_t)row * N + col, acc[r][i]);
         }
+}
+
+// BDOK: the block-diagonal form unless the blob's trailer flags a NaN weight
+// scale (a uniform branch at the start).
+template <int RT, int KP, bool BF16, bool BDOK>
+__global__ __launch_bounds__(kMxWaves * 64) void mx_stream_kernel(
+    const uint8_t* __restrict__ X, const uint8_t* __restrict__ XS, const uint8_t* __restrict__ blob,
+    void* __restrict__ Y, int M, int N, int K, size_t s_off, size_t t_off) {
+    extern __shared__ float red[];
+    if constexpr (BDOK) {
+        const uint32_t flags =
+            __builtin_amdgcn_readfirstlane(*(const uint32_t*)(blob + t_off + 8));
+        if (flags & kTrailerFlagNanScale)
+            stream_body<RT, KP, BF16, false>(X, XS, blob, Y, M, N, K, s_off, red);
+        else
+            stream_body<RT, KP, BF16, true>(X, XS, blob, Y, M, N, K, s_off, red);
+    } else {
+        stream_body<RT, KP, BF16, false>(X, XS, blob, Y, M, N, K, s_off, red);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -416,8 +493,18 @@ __global__ __launch_bounds__(kMxWaves * 64) void mx_tiled_kernel(
 template <int RT, int KP>
 hipError_t launch_stream_t(const uint8_t* xq, const uint8_t* xs, const void* packed, void* Y,
                            int64_t M, const LayoutMX& L, const PlanMX& plan, hipStream_t stream) {
-    mx_stream_kernel<RT, KP, MXFP4_TU_BF16 != 0><<<plan.grid, kMxWaves * 64, plan.lds, stream>>>(
-        xq, xs, (const uint8_t*)packed, Y, (int)M, (int)L.N, (int)L.K, L.s_off);
+    constexpr bool BF = MXFP4_TU_BF16 != 0;
+    if constexpr (RT == 1) {
+        if (plan.bd) {
+            if (M > kMxBlockDiagMaxRows || M * L.K > kMxBlockDiagMaxXBytes)
+                return hipErrorInvalidValue;   // the plan never asks for it
+            mx_stream_kernel<1, KP, BF, true><<<plan.grid, kMxWaves * 64, plan.lds, stream>>>(
+                xq, xs, (const uint8_t*)packed, Y, (int)M, (int)L.N, (int)L.K, L.s_off, L.t_off);
+            return hipGetLastError();
+        }
+    }
+    mx_stream_kernel<RT, KP, BF, false><<<plan.grid, kMxWaves * 64, plan.lds, stream>>>(
+        xq, xs, (const uint8_t*)packed, Y, (int)M, (int)L.N, (int)L.K, L.s_off, L.t_off);
     return hipGetLastError();
 }
 

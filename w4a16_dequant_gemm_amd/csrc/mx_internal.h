@@ -22,7 +22,8 @@
 // Region S (K*N/32 bytes): per (tile t, quad q of 4 k-steps) 64 lanes x 4
 //   bytes at ((t*KQ + q)*64 + l)*4: byte u is the scale of column 32t + l%32,
 //   block 2*(4q + u) + l/32, i.e. lane l's B scale for k-step 4q + u.
-// Trailer (16 bytes): magic, layout version, 0, 32 (the block size).
+// Trailer (16 bytes): magic, layout version, flags, 32 (the block size);
+// flag bit 0: some weight block scale is 0xFF (the E8M0 NaN).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stddef.h>
@@ -38,6 +39,7 @@ constexpr int kKAlign = 256;
 constexpr int kNAlign = 128;
 constexpr int kTrailerBytes = 16;
 constexpr uint32_t kTrailerMagic = 0x3450464Du;   // "MFP4"
+constexpr uint32_t kTrailerFlagNanScale = 1u;
 
 struct LayoutMX {
     int64_t K, N, NT, KS, KQ;
@@ -63,12 +65,16 @@ enum VariantMX { MX_STREAM = 0, MX_TILED = 1 };
 constexpr int kMxWaves = 8;
 constexpr int kMxStreamMaxRows = 64;
 constexpr int kMxStreamDefaultRows = 32;
+constexpr int kMxBlockDiagMaxRows = 8;   // streaming kernel on the 16x16x128 form
+// ... while M * K, its X bytes, stays below this (32-bit buffer offsets)
+constexpr int64_t kMxBlockDiagMaxXBytes = (int64_t)1 << 30;
 constexpr int kMxRowBytes = 80;   // 64 bytes of X per row and k-step + 16 of padding
 
 struct PlanMX {
     VariantMX variant;
     int rt;          // 32-row tiles per wave
     int kp;          // STREAM: parts of K per tile
+    bool bd;         // STREAM: the 16x16x128 block-diagonal form (M <= 4)
     int cfg;         // TILED: workgroup tile 0 = 256 x 256, 1 = 128 x 128, 2 = 256 x 128,
                      // 3 = 256 x 256 with two k-steps per LDS stage
     int grid;

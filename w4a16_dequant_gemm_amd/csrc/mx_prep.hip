@@ -30,8 +30,10 @@ __global__ void mx_repack_words(const uint32_t* __restrict__ qweight, uint32_t* 
     out[idx] = qweight[row * N + col];
 }
 
+// A scale of 0xFF (the E8M0 NaN) is flagged in the trailer, which is written
+// before this kernel runs.
 __global__ void mx_repack_scales(const uint8_t* __restrict__ ws, uint8_t* __restrict__ out,
-                                 int64_t N, int64_t KQ, int64_t nbytes) {
+                                 int64_t N, int64_t KQ, int64_t nbytes, uint32_t* __restrict__ trailer) {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= nbytes) return;
     const int u = (int)(idx & 3);
@@ -40,7 +42,9 @@ __global__ void mx_repack_scales(const uint8_t* __restrict__ ws, uint8_t* __rest
     const int64_t q = quad % KQ;
     const int64_t t = quad / KQ;
     const int64_t block = 2 * (4 * q + u) + (lane >> 5);
-    out[idx] = ws[block * N + t * kTileCols + (lane & 31)];
+    const uint8_t v = ws[block * N + t * kTileCols + (lane & 31)];
+    out[idx] = v;
+    if (v == 0xFFu) atomicOr(trailer + 2, kTrailerFlagNanScale);
 }
 
 __global__ void mx_init_trailer(uint32_t* __restrict__ trailer) {
@@ -119,9 +123,11 @@ hipError_t launch_mx_repack(const uint32_t* qweight, const uint8_t* ws, const La
     const int64_t nwords = (int64_t)(L.w_bytes / 4);
     mx_repack_words<<<blocks_for(nwords, 256), 256, 0, stream>>>(qweight, (uint32_t*)base, L.N,
                                                                  L.KS, nwords);
+    uint32_t* trailer = (uint32_t*)(base + L.t_off);
+    mx_init_trailer<<<1, 1, 0, stream>>>(trailer);
     const int64_t nsc = (int64_t)L.s_bytes;
-    mx_repack_scales<<<blocks_for(nsc, 256), 256, 0, stream>>>(ws, base + L.s_off, L.N, L.KQ, nsc);
-    mx_init_trailer<<<1, 1, 0, stream>>>((uint32_t*)(base + L.t_off));
+    mx_repack_scales<<<blocks_for(nsc, 256), 256, 0, stream>>>(ws, base + L.s_off, L.N, L.KQ, nsc,
+                                                               trailer);
     return hipGetLastError();
 }
 

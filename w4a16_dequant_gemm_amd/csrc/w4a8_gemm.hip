@@ -111,7 +111,7 @@ __global__ __launch_bounds__(kW8Waves * 64) void w8_stream_kernel(
         const int ai = lane & 15;
         const int axr = (ai & 3) + 4 * (ai >> 3);
         const bool alive = ((ai >> 2) & 1) == ((lane >> 4) & 1) && axr < M;
-        xoff = alive ? (uint32_t)(axr * K + 16 * (lane >> 5)) : kPastEnd;
+        xoff = alive ? (uint32_t)axr * (uint32_t)K + 16u * (uint32_t)(lane >> 5) : kPastEnd;
     }
 
     Acc acc[RT];
