@@ -586,7 +586,6 @@ __global__ __launch_bounds__(kW8Waves * 64) void w8_coop_kernel(
     constexpr int CK = 2;                               // chunks per LDS stage
     constexpr int NTB = WN * CT;                        // column tiles per workgroup (8)
     constexpr int BM = WM * RT * 32;
-    constexpr int BN = NTB * 32;
     constexpr int RB = 64 * CK + 16;
     constexpr int XBYTES = BM * RB;
     constexpr int BBYTES = NTB * CK * 2 * 1024;         // [tile][chunk][k-step][lane] 16 B
