@@ -167,6 +167,11 @@ __device__ __forceinline__ void reset_counter(uint32_t* counter) {
 constexpr int SK_WAVES = kSplitKWaves;
 constexpr int SK_U = kSplitKBatch;
 constexpr int SK_NBUF = 2;   // batches held in registers per wave
+// The 8-row split-K form reads X through a buffer resource: its lanes with
+// an empty A block use an offset past the end (zeros); X's bytes stay at most
+// kBdMaxXBytes so that every offset fits 32 bits.
+constexpr uint32_t kBdPastEnd = 0x40000000u;
+constexpr int64_t kBdMaxXBytes = (int64_t)1 << 30;
 
 // Balanced contiguous split of TB batches over the grid's waves: wave gw
 // starts at gw*base + min(gw, rem) and owns base (+1 if gw < rem) batches.
@@ -226,6 +231,22 @@ __global__ __launch_bounds__(SK_WAVES * 64) void splitk_kernel(
     // feed accumulator rows that are never stored), 8 halves at 8*(lane/32).
     const int arow = min(lane & 31, M - 1);
     const uint16_t* xlane = X + (size_t)arow * K + 8 * (lane >> 5);
+    // MB = 8: v_mfma_f32_16x16x32 with a block-diagonal A operand, as in the
+    // decode kernel (half the matrix-core cycles on the same B operands):
+    // lane l is A row i = l % 16 of slot l / 16, X row i % 4 + 4 * (i / 8)
+    // if row i's tile half (i / 4) % 2 is the slot's (l / 16) % 2 and that
+    // row is < M; other lanes read zeros past the end of a buffer resource
+    // over X.  The launcher uses it only while M * K * 2 <= 2^30.
+    constexpr bool BD = MB == 8;
+    const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)X, (short)0, BD ? M * K * 2 : 0, kBufferRsrcWord3);
+    uint32_t xoff = 0;
+    if constexpr (BD) {
+        const int ai = lane & 15;
+        const int axr = (ai & 3) + 4 * (ai >> 3);
+        const bool alive = ((ai >> 2) & 1) == ((lane >> 4) & 1) && axr < M;
+        xoff = alive ? 2u * ((uint32_t)axr * (uint32_t)K + 8u * (uint32_t)(lane >> 5)) : kBdPastEnd;
+    }
     const int c32 = lane & 31;
     const uint32_t lane16 = (uint32_t)lane * 16;
 
@@ -258,7 +279,14 @@ __global__ __launch_bounds__(SK_WAVES * 64) void splitk_kernel(
                                        : (const u32x4*)xlane);
         }
 #pragma unroll
-        for (int u = 0; u < SK_U; ++u) b.x[u] = *(const u32x4*)(xlane + (size_t)(4 * c + u) * kKStep);
+        for (int u = 0; u < SK_U; ++u) {
+            if constexpr (BD)
+                b.x[u] = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                               xrs, xoff + (uint32_t)(4 * c + u) * (2 * kKStep), 0, 0));
+            else
+                b.x[u] = *(const u32x4*)(xlane + (size_t)(4 * c + u) * kKStep);
+        }
         ++issued;
         if (++iL == nbat) {
             iL = 0;
@@ -266,9 +294,10 @@ __global__ __launch_bounds__(SK_WAVES * 64) void splitk_kernel(
         }
     };
 
-    f32x16 acc[4];
+    using Acc = typename std::conditional<BD, f32x4, f32x16>::type;
+    Acc acc[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[t] = f32x16{};
+    for (int t = 0; t < 4; ++t) acc[t] = Acc{};
     const Magic mg = make_magic();
     const uint32_t zsh = zent_shift<G>(c32);   // this lane's zero entry in its dword
 
@@ -287,7 +316,10 @@ __global__ __launch_bounds__(SK_WAVES * 64) void splitk_kernel(
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const u32x4 bop = dequant_sel<decltype(ex)::value>(b.w[t][u], prm[t], mg);
-                acc[t] = mfma32x32x16<DT>(b.x[u], bop, acc[t]);
+                if constexpr (BD)
+                    acc[t] = mfma16x16x32<DT>(b.x[u], bop, acc[t]);
+                else
+                    acc[t] = mfma32x32x16<DT>(b.x[u], bop, acc[t]);
             }
         }
     };
@@ -367,7 +399,7 @@ __global__ __launch_bounds__(SK_WAVES * 64) void splitk_kernel(
                         }
                         if (!range_end) {
 #pragma unroll
-                            for (int t = 0; t < 4; ++t) acc[t] = f32x16{};
+                            for (int t = 0; t < 4; ++t) acc[t] = Acc{};
                         }
                     }
                     if (++iC == nbat) {
@@ -895,7 +927,9 @@ template <int DT, bool SYM, int GS>
 void launch_splitk(const void* X, const void* packed, void* Y, int64_t M, const Layout& L,
                    const Plan& p, float* part, uint32_t* cnt, hipStream_t stream,
                    const Epilogue& ep) {
-    if (M <= 8) launch_splitk_mb<DT, SYM, GS, 8>(X, packed, Y, M, L, p, part, cnt, stream, ep);
+    // the 8-row form addresses X with 32-bit buffer offsets
+    if (M <= 8 && M * L.K * 2 <= kBdMaxXBytes)
+        launch_splitk_mb<DT, SYM, GS, 8>(X, packed, Y, M, L, p, part, cnt, stream, ep);
     else if (M <= 16) launch_splitk_mb<DT, SYM, GS, 16>(X, packed, Y, M, L, p, part, cnt, stream, ep);
     else launch_splitk_mb<DT, SYM, GS, 32>(X, packed, Y, M, L, p, part, cnt, stream, ep);
 }
