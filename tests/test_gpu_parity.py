@@ -313,6 +313,21 @@ def test_full_size_workload(name):
     assert same_bits(got, want)
 
 
+@pytest.mark.parametrize("M,dtype,sym", [(3, "fp16", False), (8, "bf16", True), (8, "fp16", False)])
+def test_full_size_ffn_down_small_m(M, dtype, sym):
+    """The FFN-down shape (K = 28672, N = 8192) at decode M: X does not fit the
+    decode kernel's LDS, so the default plan runs the split-K kernel's 8-row
+    (block-diagonal 16x16x32) form; every output is compared with the oracle."""
+    lib()
+    K, N, G = 28672, 8192, 128
+    p = synth.make_problem(M, K, N, G, dtype, sym, seed=11 + M, outlier_frac=0.001)
+    say(f"full-size FFN-down M={M} {dtype} sym={sym}")
+    d = OnDevice(p)
+    Y = d.gemm()
+    Yref, B = oracle.gemm(p.X, p.qweight, p.scales, p.zeros, M, N, K, G, dtype, sym)
+    assert_gemm_close(p, d.y_float(Y), Yref, B, f"FFN-down M={M}")
+
+
 @pytest.mark.parametrize("nbytes", [1024, 3 * (1 << 20) + 5 * 1024, 117440512])
 def test_read_probe_reads_every_byte_once(nbytes):
     """The read-bandwidth probe behind the benchmark's ceiling: XOR of its
