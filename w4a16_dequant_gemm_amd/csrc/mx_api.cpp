@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/mxfp4.h"
 #include "mx_internal.h"
 
@@ -18,6 +20,23 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 w4a16_status_t from_hip(hipError_t e) { return e == hipSuccess ? W4A16_OK : W4A16_ERR_HIP; }
 
+constexpr int kDefaultCUs = 256;
+constexpr int kMaxDevices = 64;
+
+// Compute units of the current device, read once per device.
+int num_cus() {
+    static std::atomic<int> cache[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return kDefaultCUs;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+        n = kDefaultCUs;
+    cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
 w4a16_status_t check_kn(int64_t K, int64_t N) {
     if (K < 1 || N < 1 || K >= kMaxDim || N >= kMaxDim) return W4A16_ERR_INVALID_ARG;
     if ((double)K * (double)N >= (double)((int64_t)1 << 40)) return W4A16_ERR_INVALID_ARG;
@@ -27,7 +46,7 @@ w4a16_status_t check_kn(int64_t K, int64_t N) {
 
 }  // namespace
 
-PlanMX make_plan_mx(int64_t M, int64_t N, int64_t K, uint32_t flags) {
+PlanMX make_plan_mx(int64_t M, int64_t N, int64_t K, uint32_t flags, int cus) {
     PlanMX p{};
     const uint32_t hint = flags & MXFP4_PLAN_MASK;
     const int param = (int)((flags >> W4A16_PLAN_PARAM_SHIFT) & 0xFFu);
@@ -39,10 +58,24 @@ PlanMX make_plan_mx(int64_t M, int64_t N, int64_t K, uint32_t flags) {
     if (stream) {
         p.variant = MX_STREAM;
         p.rt = M <= 32 ? 1 : 2;
-        // parts of K per tile, measured on the 8192 x 28672 layer: 4 for
-        // M <= 8 (28.6 us at M = 1 against 29.6 with 8), 2 above (36.8 us at
-        // M = 16 against 39.6 with 4)
-        p.kp = (param == 2 || param == 4 || param == 8) && KS >= param ? param : (M <= 8 ? 4 : 2);
+        // parts of K per tile.  M <= 8: the most parts whose workgroups are
+        // all resident at two per CU (measured, us per call: 8192 x 28672,
+        // 896 tiles, 4 parts 28.7 vs 29.2 with 8; 8192 x 8192, 256 tiles, 8
+        // parts 11.2 vs 17.1 with 4; 28672 x 8192 31.4 vs 53.4).  M > 8: 2
+        // parts (36.8 us at M = 16 on 8192 x 28672 against 39.6 with 4),
+        // more while fewer than 3/4 of the CUs would get a workgroup (8192 x
+        // 8192: M = 16 13.0 with 8 vs 34.8 with 2, M = 32 18.8 vs 47.2).
+        int kp = 2;
+        if (M <= 8) {
+            for (int c = 8; c >= 2; c /= 2)
+                if (NT * c / kMxWaves <= 2 * (int64_t)cus && KS >= c) {
+                    kp = c;
+                    break;
+                }
+        } else {
+            while (kp < 8 && NT * kp / kMxWaves < (int64_t)cus * 3 / 4 && KS >= 2 * kp) kp *= 2;
+        }
+        p.kp = (param == 2 || param == 4 || param == 8) && KS >= param ? param : kp;
         // block-diagonal 16x16x128 form, measured on the 8192 x 28672 layer
         // (us per call, same box): M = 1 28.9 vs 30.1, M = 2 28.8 vs 30.0,
         // M = 4 30.5 vs 30.8, but M = 8 34.6 vs 31.5
@@ -112,7 +145,7 @@ w4a16_status_t mxfp4_gemm(const uint8_t* xq, const uint8_t* xs, const void* pack
         return W4A16_ERR_INVALID_ARG;
     const LayoutMX L = make_layout_mx(K, N);
     if (packed_bytes < L.total) return W4A16_ERR_INVALID_ARG;
-    const PlanMX plan = make_plan_mx(M, N, K, flags);
+    const PlanMX plan = make_plan_mx(M, N, K, flags, num_cus());
     hipStream_t s = (hipStream_t)stream;
     const hipError_t e = (flags & MXFP4_BF16) ? launch_mx_gemm_bf16(xq, xs, packed, Y, M, L, plan, s)
                                               : launch_mx_gemm_f16(xq, xs, packed, Y, M, L, plan, s);

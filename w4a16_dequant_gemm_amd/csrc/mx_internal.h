@@ -82,7 +82,7 @@ struct PlanMX {
     size_t lds;
 };
 
-PlanMX make_plan_mx(int64_t M, int64_t N, int64_t K, uint32_t flags);
+PlanMX make_plan_mx(int64_t M, int64_t N, int64_t K, uint32_t flags, int cus);
 
 hipError_t launch_mx_repack(const uint32_t* qweight, const uint8_t* ws, const LayoutMX& L,
                             void* packed, hipStream_t stream);

@@ -63,14 +63,22 @@ PlanW8 make_plan_w8(int64_t M, int64_t N, int64_t K, uint32_t flags, int cus) {
         if ((param == 2 || param == 4 || param == 8) && KC >= param) {
             p.kp = param;
         } else {
-            // M <= 8: the fewest parts that still give two workgroups per CU;
-            // M > 8: 4 parts (measured fastest on the 8192 x 28672 layer)
-            p.kp = KC >= 8 ? 8 : 4;
+            // M <= 8: the most parts whose workgroups are all resident at
+            // two per CU.  Measured (us per call, same box): 8192 x 28672
+            // (896 tiles) M = 1 28.3 with 4 parts (448 workgroups) vs 29.1-30.6
+            // with 8, M = 4 29.6 vs 31.4; 8192 x 8192 (256 tiles) 11.5 with 8
+            // vs 17.6 with 4.  M > 8: 4 parts (measured fastest on the
+            // 8192 x 28672 layer), more while fewer than 3/4 of the CUs would
+            // get a workgroup (8192 x 8192: M = 16 13.8 with 8 vs 20.3 with
+            // 4, M = 32 18.9 vs 27.6).
+            p.kp = 2;
             if (M > 8) {
-                p.kp = 4;
+                p.kp = KC >= 4 ? 4 : 2;
+                while (p.kp < 8 && NT * p.kp / kW8Waves < (int64_t)cus * 3 / 4 && KC >= 2 * p.kp)
+                    p.kp *= 2;
             } else {
-                for (int kp = 2; kp <= 8; kp *= 2)
-                    if (NT * kp / kW8Waves >= 2 * (int64_t)cus && KC >= kp) {
+                for (int kp = 8; kp >= 2; kp /= 2)
+                    if (NT * kp / kW8Waves <= 2 * (int64_t)cus && KC >= kp) {
                         p.kp = kp;
                         break;
                     }
